@@ -1,0 +1,238 @@
+"""Benchmark of the differential-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+per-head lambda for both workloads, the fused V1 prefill (with the per-head
+RMS-norm epilogue) of the long multi-needle workload (B=1, 32 heads,
+N=65536, d=64, dv=128, layer 12), and the V2 split-KV decode of the GQA
+workload (B=32, 32 query heads over 8 KV heads, D=128, lengths uniform in
+[4096, 65536]).  Inputs are generated on the GPU and resident in HBM before
+the timed region.
+
+Prints one JSON line: whole-step algorithmic TFLOP/s as `value`, the prefill
+kernel against the bf16 matrix-core roofline, the decode kernels against the
+HBM roofline, and the CPU oracle timed on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "diff-attn prefill TFLOP/s & decode HBM GB/s, % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E peak
+
+
+def prefill_flops(case) -> float:
+    """Algorithmic flops: per visible (query, key) pair, two d-long dot
+    products and one dv-wide weighted accumulation: 4d + 2dv."""
+    return float(case.pairs()) * (4 * case.d + 2 * case.dv)
+
+
+def decode_bytes(case, lens) -> float:
+    """Algorithmic HBM bytes: every visible K and V row once (bf16), plus q,
+    lambda, lengths and the fp32 output."""
+    kv = float(sum(int(x) for x in lens)) * case.Hkv * 2 * case.D * 2
+    return kv + case.B * case.Hq * case.D * 2 + (case.Hq // 2) * 4 + case.B * 4 + \
+        case.B * (case.Hq // 2) * case.D * 4
+
+
+def decode_flops(case, lens) -> float:
+    """Per visible key and pair: two D-long dots and one D-wide accumulation."""
+    return float(sum(int(x) for x in lens)) * (case.Hq // 2) * 6 * case.D
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill", default="multineedle_64k",
+                    choices=["multineedle_64k", "needle_32k", "v1_norm"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from differential_attention_prefill_amd import api
+    from differential_attention_prefill_amd import workloads as W
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    api.load_library()
+    pcase = {"multineedle_64k": W.MULTI_NEEDLE_64K, "needle_32k": W.NEEDLE_32K,
+             "v1_norm": W.V1_NORM}[args.prefill]
+    dcase = W.V2_DECODE
+    print("# generating inputs: %s + %s" % (pcase.name, dcase.name), file=sys.stderr, flush=True)
+    pin = W.make_prefill(pcase, device=dev)
+    din = W.make_decode(dcase, device=dev)
+    d = pcase.d
+    q1, q2 = pin["q"][..., :d], pin["q"][..., d:]
+    k1, k2 = pin["k"][..., :d], pin["k"][..., d:]
+    v = pin["v"]
+    plam_in = [pin[k].contiguous() for k in ("lq1", "lk1", "lq2", "lk2")]
+    dlam_in = [din[k].contiguous() for k in ("lq1", "lk1", "lq2", "lk2")]
+    plam = torch.empty(pcase.H, dtype=torch.float32, device=dev)
+    dlam = torch.empty(dcase.Hq // 2, dtype=torch.float32, device=dev)
+    pout = torch.empty((pcase.B, pcase.H, pcase.N, pcase.dv), dtype=torch.float32, device=dev)
+    dout = torch.empty((dcase.B, dcase.Hq // 2, dcase.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(api.diffattn_decode_workspace_bytes(dcase.B, dcase.Hq, dcase.Hkv, dcase.D,
+                                                         dcase.Lmax), dtype=torch.uint8, device=dev)
+    norm_scale = (1.0 - api.diffattn_lambda_init(pcase.layer)) if pcase.rmsnorm else 1.0
+    lens = din["seq_lens"].cpu().tolist()
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(record):
+        if record:
+            ev[0].record()
+        api.diffattn_lambda(*plam_in, layer=pcase.layer, out=plam)
+        api.diffattn_lambda(*dlam_in, layer=dcase.layer, out=dlam)
+        if record:
+            ev[1].record()
+        api.diffattn_prefill(q1, q2, k1, k2, v, plam, causal=pcase.causal, rmsnorm=pcase.rmsnorm,
+                             eps=pcase.eps, norm_scale=norm_scale, out=pout)
+        if record:
+            ev[2].record()
+        api.diffattn_decode(din["q"], din["k_cache"], din["v_cache"], din["seq_lens"], dlam,
+                            workspace=ws, out=dout)
+        if record:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(False)
+        print("# warmup step %d done" % i, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+
+    t_lam, t_pre, t_dec = [], [], []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()   # per-step sync keeps the event pairs readable
+        t_lam.append(ev[0].elapsed_time(ev[1]))
+        t_pre.append(ev[1].elapsed_time(ev[2]))
+        t_dec.append(ev[2].elapsed_time(ev[3]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print("# timed %d steps in %.3f s" % (args.steps, wall), file=sys.stderr, flush=True)
+
+    ms_step = 1e3 * wall / args.steps
+    fp = prefill_flops(pcase)
+    fd = decode_flops(dcase, lens)
+    bd = decode_bytes(dcase, lens)
+    pre_ms = float(np.mean(t_pre))
+    dec_ms = float(np.mean(t_dec))
+    pre_tflops = fp / (pre_ms * 1e-3) / 1e12
+    dec_gbps = bd / (dec_ms * 1e-3) / 1e9
+    value = (fp + fd) / (ms_step * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s prefill + %s decode" % (pcase.name, dcase.name),
+            "prefill": {"B": pcase.B, "H": pcase.H, "N": pcase.N, "d": pcase.d, "dv": pcase.dv,
+                        "causal": pcase.causal, "rmsnorm": pcase.rmsnorm, "layer": pcase.layer},
+            "decode": {"B": dcase.B, "Hq": dcase.Hq, "Hkv": dcase.Hkv, "D": dcase.D,
+                       "max_len": dcase.Lmax, "sum_len": int(sum(lens))},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_bf16_kernel<64,128,4>",
+            "achieved": round(pre_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": fp,
+            "avg_launch_ms": round(pre_ms, 4),
+        },
+        "decode": {
+            "bound": "hbm",
+            "achieved": round(dec_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes_per_launch": bd,
+            "avg_launch_ms": round(dec_ms, 4),
+        },
+        "lambda_avg_ms": round(float(np.mean(t_lam)), 4),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(pcase, pin, dcase, din, plam, dlam, norm_scale,
+                                              args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(pcase, pin, dcase, din, plam, dlam, norm_scale, target_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same step:
+    uniformly drawn prefill query rows, plus the decode of a few sequences."""
+    import numpy as np
+
+    import oracle
+
+    d = pcase.d
+    q, k, v = (pin[x].cpu() for x in ("q", "k", "v"))
+    q1, q2 = q[..., :d].contiguous(), q[..., d:].contiguous()
+    k1, k2 = k[..., :d].contiguous(), k[..., d:].contiguous()
+    v = v.contiguous()
+    lam = plam.cpu().numpy()
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(0)
+    total_rows = pcase.B * pcase.H * pcase.N
+    per_pair = 4 * pcase.d + 2 * pcase.dv
+
+    def run_rows(n):
+        rows = rng.integers(0, total_rows, size=n).astype(np.int64)
+        flops = float(((rows % pcase.N) + 1).sum()) * per_pair
+        t = time.perf_counter()
+        oracle.prefill(q1, q2, k1, k2, v, lam, causal=True, rmsnorm=pcase.rmsnorm, eps=pcase.eps,
+                       norm_scale=norm_scale, rows=rows, nthreads=threads)
+        return flops, time.perf_counter() - t
+
+    f0, t0 = run_rows(4 * threads)                 # calibration
+    rate = f0 / max(t0, 1e-6)
+    n = max(threads, int(0.8 * target_s * rate / (pcase.N / 2.0 * per_pair)))
+    f1, t1 = run_rows(n)
+    # Decode: the first two sequences, all pairs.
+    nb = 2
+    t = time.perf_counter()
+    oracle.decode(din["q"][:nb].cpu(), din["k_cache"][:nb].cpu(), din["v_cache"][:nb].cpu(),
+                  din["seq_lens"][:nb].cpu(), dlam.cpu().numpy(), nthreads=threads)
+    t2 = time.perf_counter() - t
+    f2 = float(din["seq_lens"][:nb].sum().item()) * (dcase.Hq // 2) * 6 * dcase.D
+    value = (f0 + f1 + f2) / (t0 + t1 + t2) / 1e12
+    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(t0 + t1 + t2, 2),
+            "sample": "%d uniformly drawn query rows of the %d prefill rows (all their visible "
+                      "keys, with the norm epilogue) + the decode of the first %d sequences; "
+                      "fp64 C oracle, %d threads" % (4 * threads + n, total_rows, nb, threads)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+"""ctypes binding of libdiffattn (include/diffattn.h), same entry-point names.
+
+Argument marshalling only: tensor checks, pointers, strides and the current
+torch stream go in; every step of the computation runs in the library's HIP
+kernels.  PyTorch provides device memory and streams.  If the library is not
+built, every call raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdiffattn.so")
+
+DIFFATTN_FP32 = 0
+DIFFATTN_BF16 = 1
+
+STATUS = {0: "DIFFATTN_OK", 1: "DIFFATTN_ERR_INVALID_ARGUMENT", 2: "DIFFATTN_ERR_UNSUPPORTED",
+          3: "DIFFATTN_ERR_WORKSPACE", 4: "DIFFATTN_ERR_HIP"}
+
+EXPORTS = ("diffattn_lambda_init", "diffattn_lambda", "diffattn_prefill",
+           "diffattn_decode_workspace_bytes", "diffattn_decode", "diffattn_status_string",
+           "diffattn_last_error")
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__("%s: %s" % (STATUS.get(status, str(status)), detail))
+
+
+_lib = None
+
+
+def load_library():
+    """Load libdiffattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libdiffattn.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, L, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.diffattn_lambda_init.restype = ctypes.c_double
+    lib.diffattn_lambda_init.argtypes = [I]
+    lib.diffattn_lambda.restype = I
+    lib.diffattn_lambda.argtypes = [P, P, P, P, I, I, I, P, P]
+    lib.diffattn_prefill.restype = I
+    lib.diffattn_prefill.argtypes = [P, P, P, P, P, L, L, L, I, I, I, I, I, I, I, P, I, F, F, P,
+                                     P, P]
+    lib.diffattn_decode_workspace_bytes.restype = S
+    lib.diffattn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.diffattn_decode.restype = I
+    lib.diffattn_decode.argtypes = [P, P, P, P, I, I, I, I, I, P, P, S, P, P]
+    lib.diffattn_status_string.restype = ctypes.c_char_p
+    lib.diffattn_status_string.argtypes = [I]
+    lib.diffattn_last_error.restype = ctypes.c_char_p
+    lib.diffattn_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise DiffAttnError(status, load_library().diffattn_last_error().decode())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _token_stride(t: torch.Tensor, name: str) -> int:
+    """ld of a [B, H, N, w] tensor laid out as [B][H][N][ld] with unit channel stride."""
+    if t.dim() != 4:
+        raise ValueError("%s must be [B, H, N, width]" % name)
+    B, H, N, w = t.shape
+    sb, sh, sn, sc = t.stride()
+    if sc != 1 and w > 1:
+        raise ValueError("%s must have unit stride along its last dimension" % name)
+    ld = sn
+    if (H > 1 and sh != N * ld) or (B > 1 and sb != H * N * ld):
+        raise ValueError("%s must be laid out [B][H][N][ld] (head stride N*ld)" % name)
+    return ld
+
+
+# --------------------------------------------------------------------------
+# Entry points
+# --------------------------------------------------------------------------
+
+def diffattn_lambda_init(layer: int) -> float:
+    return float(load_library().diffattn_lambda_init(int(layer)))
+
+
+def diffattn_lambda(lq1, lk1, lq2, lk2, layer: int, out=None, stream=None) -> torch.Tensor:
+    """Per-head lambda, fp32 [H]; inputs fp32 [H, dim] on the GPU."""
+    lib = load_library()
+    for t in (lq1, lk1, lq2, lk2):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != lq1.shape:
+            raise ValueError("lq1, lk1, lq2, lk2 must be contiguous fp32 tensors of one shape")
+    H, dim = (1, lq1.shape[0]) if lq1.dim() == 1 else lq1.shape
+    if out is None:
+        out = torch.empty(H, dtype=torch.float32, device=lq1.device)
+    _check(lib.diffattn_lambda(_ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), H, dim, int(layer),
+                               _ptr(out), _stream(stream)))
+    return out
+
+
+def diffattn_prefill(q1, q2, k1, k2, v, lam, *, causal: bool = True, rmsnorm: bool = False,
+                     eps: float = 1e-5, norm_scale: float = 1.0, norm_weight=None, out=None,
+                     stream=None) -> torch.Tensor:
+    """Fused differential-attention prefill; returns fp32 [B, H, N, dv].
+
+    q1, q2, k1, k2: [B, H, N, d] views (e.g. halves of a packed [B, H, N, 2d]
+    tensor), v: [B, H, N, dv], all fp32 or all bf16; lam: fp32 [H].
+    """
+    lib = load_library()
+    if q1.dtype == torch.bfloat16:
+        dt = DIFFATTN_BF16
+    elif q1.dtype == torch.float32:
+        dt = DIFFATTN_FP32
+    else:
+        raise ValueError("prefill inputs must be bf16 or fp32")
+    for t in (q2, k1, k2, v):
+        if t.dtype != q1.dtype:
+            raise ValueError("q1, q2, k1, k2, v must share one dtype")
+    B, H, N, d = q1.shape
+    dv = v.shape[-1]
+    for t, name in ((q2, "q2"), (k1, "k1"), (k2, "k2")):
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError("%s must be [B, H, N, d] like q1" % name)
+    if tuple(v.shape[:3]) != (B, H, N):
+        raise ValueError("v must be [B, H, N, dv]")
+    ldq, ldq2 = _token_stride(q1, "q1"), _token_stride(q2, "q2")
+    ldk, ldk2 = _token_stride(k1, "k1"), _token_stride(k2, "k2")
+    ldv = _token_stride(v, "v")
+    if ldq != ldq2 or ldk != ldk2:
+        raise ValueError("q1/q2 and k1/k2 must share their token strides")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=torch.float32, device=q1.device)
+    _check(lib.diffattn_prefill(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), ldq, ldk, ldv, dt,
+                                B, H, N, d, dv, int(bool(causal)), _ptr(lam), int(bool(rmsnorm)),
+                                float(eps), float(norm_scale), _ptr(norm_weight), _ptr(out),
+                                _stream(stream)))
+    return out
+
+
+def diffattn_prefill_packed(q, k, v, lam, **kw) -> torch.Tensor:
+    """Prefill on packed V1 tensors q, k: [B, H, N, 2d] (halves Q1|Q2, K1|K2)."""
+    d = q.shape[-1] // 2
+    return diffattn_prefill(q[..., :d], q[..., d:], k[..., :d], k[..., d:], v, lam, **kw)
+
+
+def diffattn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_len: int) -> int:
+    return int(load_library().diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len))
+
+
+def diffattn_decode(q, k_cache, v_cache, seq_lens, lam, *, workspace=None, out=None,
+                    stream=None) -> torch.Tensor:
+    """V2-layout decode; returns fp32 [B, Hq/2, D].
+
+    q: bf16 [B, Hq, D]; k_cache, v_cache: bf16 [B, Hkv, max_len, D]; seq_lens:
+    int32 [B]; lam: fp32 [Hq/2]; workspace: optional uint8 device tensor of at
+    least diffattn_decode_workspace_bytes(...) bytes.
+    """
+    lib = load_library()
+    B, Hq, D = q.shape
+    _, Hkv, max_len, _ = k_cache.shape
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if seq_lens.dtype != torch.int32 or lam.dtype != torch.float32:
+        raise ValueError("seq_lens must be int32 and lambda fp32")
+    need = diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq // 2, D), dtype=torch.float32, device=q.device)
+    _check(lib.diffattn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv,
+                               D, max_len, _ptr(lam), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(out),
+                               _stream(stream)))
+    return out

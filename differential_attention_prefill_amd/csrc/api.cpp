@@ -1,0 +1,221 @@
+// C ABI of libdiffattn: argument validation and dispatch to the HIP kernels.
+// The contract of every entry point is documented in include/diffattn.h.
+#include "diffattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+diffattn_status_t fail(diffattn_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+diffattn_status_t ok() {
+    g_last_error[0] = '\0';
+    return DIFFATTN_OK;
+}
+
+// True if p is device (or managed) memory the current device can address.
+// Runs only after every pure-argument check, so argument errors are reported
+// without touching the HIP runtime.
+bool is_device_ptr(const void* p) {
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // an unknown pointer is not a sticky error
+        return false;
+    }
+    return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged ||
+           attr.type == hipMemoryTypeUnified;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+diffattn_status_t check_device(const void* p, const char* name) {
+    if (!is_device_ptr(p))
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s is not device memory", name);
+    return DIFFATTN_OK;
+}
+
+diffattn_status_t hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(DIFFATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+double diffattn_lambda_init(int layer) {
+    if (layer < 1) return NAN;
+    return 0.8 - 0.6 * std::exp(-0.3 * (double)(layer - 1));
+}
+
+diffattn_status_t diffattn_lambda(const float* lq1, const float* lk1, const float* lq2,
+                                  const float* lk2, int H, int dim, int layer, float* lambda_out,
+                                  void* stream) {
+    if (!lq1 || !lk1 || !lq2 || !lk2 || !lambda_out)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_lambda: null pointer");
+    if (H < 1 || dim < 1)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_lambda: H=%d dim=%d must be >= 1", H, dim);
+    if (layer < 1)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_lambda: layer=%d must be >= 1", layer);
+    const void* ptrs[5] = {lq1, lk1, lq2, lk2, lambda_out};
+    const char* names[5] = {"lq1", "lk1", "lq2", "lk2", "lambda_out"};
+    for (int i = 0; i < 5; ++i) {
+        diffattn_status_t s = check_device(ptrs[i], names[i]);
+        if (s != DIFFATTN_OK) return s;
+    }
+    return hip_status(diffattn::launch_lambda(lq1, lk1, lq2, lk2, H, dim, diffattn_lambda_init(layer),
+                                              lambda_out, (hipStream_t)stream),
+                      "diffattn_lambda launch");
+}
+
+diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k1, const void* k2,
+                                   const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
+                                   diffattn_dtype_t dtype, int B, int H, int N, int d, int dv,
+                                   int causal, const float* lambda, int rmsnorm, float eps,
+                                   float norm_scale, const float* norm_weight, float* out,
+                                   void* stream) {
+    if (!q1 || !q2 || !k1 || !k2 || !v || !lambda || !out)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: null pointer");
+    if (B < 1 || H < 1 || N < 1 || d < 1 || dv < 1)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_prefill: B=%d H=%d N=%d d=%d dv=%d must be >= 1", B, H, N, d, dv);
+    if (dtype != DIFFATTN_FP32 && dtype != DIFFATTN_BF16)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: unknown dtype %d", (int)dtype);
+    if (ldq < d || ldk < d || ldv < dv)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_prefill: strides ldq=%lld ldk=%lld ldv=%lld below widths d=%d dv=%d",
+                    (long long)ldq, (long long)ldk, (long long)ldv, d, dv);
+    const int esize = dtype == DIFFATTN_BF16 ? 2 : 4;
+    if ((ldq * esize) % 16 || (ldk * esize) % 16 || (ldv * esize) % 16)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_prefill: token strides must be multiples of 16 bytes");
+    const void* ptrs[7] = {q1, q2, k1, k2, v, out, lambda};
+    const char* names[7] = {"q1", "q2", "k1", "k2", "v", "out", "lambda"};
+    for (int i = 0; i < 6; ++i)   // vector-loaded tensors; lambda is read as scalars
+        if (!aligned16(ptrs[i]))
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: %s not 16-byte aligned",
+                        names[i]);
+    if ((reinterpret_cast<uintptr_t>(lambda) & 3u) != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: lambda not 4-byte aligned");
+    if (rmsnorm && !(eps >= 0.f))
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: eps must be >= 0");
+    const bool supported = dtype == DIFFATTN_BF16 ? diffattn::prefill_bf16_supported(d, dv)
+                                                  : diffattn::prefill_f32_supported(d, dv);
+    if (!supported)
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_prefill: (d=%d, dv=%d) not built for %s", d,
+                    dv, dtype == DIFFATTN_BF16 ? "bf16" : "fp32");
+    if ((int64_t)B * H * N > (int64_t)1 << 40)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: B*H*N too large");
+    for (int i = 0; i < 7; ++i) {
+        diffattn_status_t s = check_device(ptrs[i], names[i]);
+        if (s != DIFFATTN_OK) return s;
+    }
+    if (rmsnorm && norm_weight) {
+        diffattn_status_t s = check_device(norm_weight, "norm_weight");
+        if (s != DIFFATTN_OK) return s;
+    }
+    diffattn::PrefillArgs a;
+    a.q1 = q1; a.q2 = q2; a.k1 = k1; a.k2 = k2; a.v = v;
+    a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
+    a.B = B; a.H = H; a.N = N; a.d = d; a.dv = dv;
+    a.causal = causal ? 1 : 0;
+    a.lambda = lambda;
+    a.rmsnorm = rmsnorm ? 1 : 0;
+    a.eps = eps;
+    a.norm_scale = norm_scale;
+    a.norm_weight = rmsnorm ? norm_weight : nullptr;
+    a.out = out;
+    hipError_t e = dtype == DIFFATTN_BF16 ? diffattn::launch_prefill_bf16(a, (hipStream_t)stream)
+                                          : diffattn::launch_prefill_f32(a, (hipStream_t)stream);
+    return hip_status(e, "diffattn_prefill launch");
+}
+
+size_t diffattn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_len < 1) return 0;
+    return diffattn::decode_workspace_floats(B, Hq, D, max_len) * sizeof(float);
+}
+
+diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                  int max_len, const float* lambda, void* workspace,
+                                  size_t workspace_bytes, float* out, void* stream) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !lambda || !out)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: null pointer");
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_len < 1)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_decode: B=%d Hq=%d Hkv=%d D=%d max_len=%d must be >= 1", B, Hq, Hkv,
+                    D, max_len);
+    if (Hq % (2 * Hkv) != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_decode: Hq=%d must be a multiple of 2*Hkv=%d", Hq, 2 * Hkv);
+    const void* ptrs[6] = {q, k_cache, v_cache, seq_lens, lambda, out};
+    const char* names[6] = {"q", "k_cache", "v_cache", "seq_lens", "lambda", "out"};
+    for (int i = 0; i < 3; ++i)   // vector-loaded tensors
+        if (!aligned16(ptrs[i]))
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: %s not 16-byte aligned",
+                        names[i]);
+    for (int i = 3; i < 6; ++i)   // read or written as 4-byte scalars
+        if ((reinterpret_cast<uintptr_t>(ptrs[i]) & 3u) != 0)
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: %s not 4-byte aligned",
+                        names[i]);
+    if (!diffattn::decode_supported(D))
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_decode: head width D=%d not built", D);
+    if (Hq / Hkv > 16)
+        return fail(DIFFATTN_ERR_UNSUPPORTED,
+                    "diffattn_decode: %d query heads per KV head (at most 16)", Hq / Hkv);
+    if ((int64_t)B * Hkv * max_len > ((int64_t)1 << 40))
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: cache too large");
+    if (max_len > (1 << 30))
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: max_len too large");
+    const size_t need = diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len);
+    if (!workspace || workspace_bytes < need)
+        return fail(DIFFATTN_ERR_WORKSPACE, "diffattn_decode: workspace needs %zu bytes, got %zu",
+                    need, workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: workspace not 256-byte aligned");
+    for (int i = 0; i < 6; ++i) {
+        diffattn_status_t s = check_device(ptrs[i], names[i]);
+        if (s != DIFFATTN_OK) return s;
+    }
+    {
+        diffattn_status_t s = check_device(workspace, "workspace");
+        if (s != DIFFATTN_OK) return s;
+    }
+    diffattn::DecodeArgs a;
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.seq_lens = seq_lens;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.max_len = max_len;
+    a.lambda = lambda;
+    a.workspace = static_cast<float*>(workspace);
+    a.out = out;
+    return hip_status(diffattn::launch_decode(a, (hipStream_t)stream), "diffattn_decode launch");
+}
+
+const char* diffattn_status_string(diffattn_status_t status) {
+    switch (status) {
+        case DIFFATTN_OK: return "ok";
+        case DIFFATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case DIFFATTN_ERR_UNSUPPORTED: return "unsupported shape or type";
+        case DIFFATTN_ERR_WORKSPACE: return "workspace missing or too small";
+        case DIFFATTN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* diffattn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,302 @@
+// Split-KV differential-attention decode, V2 layout (bf16 cache, fp32 math).
+//
+// One new query token per sequence.  Pair p of a sequence uses query head 2p
+// for A1 and query head 2p+1 for A2, both over KV head g = floor(2p/(Hq/Hkv)):
+//     out_p = (softmax(q_2p K_g^T / sqrt D) - lambda_p softmax(q_2p+1 K_g^T / sqrt D)) V_g
+// (page "差分注意力" (aiknowledge.cn), "V1 到 V2 的 diff": twice the query heads
+// over the same KV heads, so one pass over the cache serves both maps and all
+// query heads of a group; part 二 Step 2 for the operator).
+//
+// The cache is read exactly once, which makes the kernel HBM-bound:
+//  - split kernel: grid (split, KV head, sequence).  A workgroup streams one
+//    chunk of DEC_CHUNK positions of K_g and V_g for ALL Hq/Hkv query heads of
+//    the group (both heads of every pair).  Each of its 4 waves takes every
+//    4th 32-key tile of the chunk.  Scores come from v_mfma_f32_16x16x32_bf16
+//    as S^T = K . Q^T (keys x query heads, the 16 columns padded with zero
+//    heads); probabilities go from registers into O^T += V^T . P^T with V^T
+//    staged through a per-wave LDS tile written transposed.  Each head keeps
+//    its own running maximum / normaliser / accumulator; the waves' states are
+//    merged in LDS and one partial state (O, m, l) per head and split is
+//    written to the workspace.
+//  - merge kernel: grid (pair, sequence).  Merges the splits of both heads of
+//    a pair by log-sum-exp weights in a fixed order (deterministic), then
+//    combines the two maps with lambda.
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int DEC_D = 128;             // head width
+constexpr int DEC_WAVES = 4;
+constexpr int DEC_THREADS = 64 * DEC_WAVES;
+constexpr int DEC_TILE = 32;           // keys per wave iteration
+constexpr int DEC_CHUNK = 1024;        // keys per split (workgroup)
+constexpr int DEC_ITERS = DEC_CHUNK / (DEC_TILE * DEC_WAVES);
+constexpr int DEC_GROUP_MAX = 16;      // query heads per KV head that fit the MFMA columns
+constexpr int DEC_VROW = DEC_TILE * 2 + 16;     // bytes per channel row of V^T (+pad)
+constexpr int DEC_VBYTES = DEC_D * DEC_VROW;    // one wave's V^T tile
+constexpr int DEC_STATE = DEC_D + 2;            // floats per partial state: O[D], m*c, l
+constexpr float DEC_TAU = 8.0f;
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Row slot rho of score tile t holds key (rho/4)*8 + t*4 + rho%4 of the
+// 32-key tile, so that the accumulator registers of tiles 0 and 1 line up as
+// 8 consecutive keys per lane group: the B operand of the next product.
+__device__ __forceinline__ int slot_key(int rho, int t) { return (rho >> 2) * 8 + t * 4 + (rho & 3); }
+
+__global__ void __launch_bounds__(DEC_THREADS)
+decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
+                    const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens, int Hq,
+                    int Hkv, int max_len, int max_splits, float* __restrict__ ws) {
+    const int split = blockIdx.x;
+    const int g = blockIdx.y;
+    const int b = blockIdx.z;
+    const int L = seq_lens[b];
+    if (L < 1 || L > max_len) return;          // the merge kernel writes zeros
+    const int c0 = split * DEC_CHUNK;
+    if (c0 >= L) return;                        // whole workgroup exits together
+    const int cend = min(L, c0 + DEC_CHUNK);
+
+    // Per-wave V^T tiles during the stream; reused as the wave-merge buffer.
+    __shared__ __attribute__((aligned(16))) unsigned char lds[DEC_WAVES * DEC_VBYTES];
+    __shared__ float merge_m[DEC_WAVES][DEC_GROUP_MAX];
+    __shared__ float merge_l[DEC_WAVES][DEC_GROUP_MAX];
+    static_assert(DEC_WAVES * DEC_GROUP_MAX * DEC_D * 4 <= DEC_WAVES * DEC_VBYTES,
+                  "merge buffer must fit in the V^T tiles");
+    float (*merge_o)[DEC_GROUP_MAX][DEC_D] = reinterpret_cast<float (*)[DEC_GROUP_MAX][DEC_D]>(lds);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 15;      // query head inside the group (MFMA column)
+    const int grp = lane >> 4;      // 4 lane groups
+    const int G = Hq / Hkv;         // query heads in this KV group
+    const bool col_ok = col < G;
+
+    const int64_t kv0 = ((int64_t)b * Hkv + g) * max_len;   // row of position 0
+    const float c = 1.4426950408889634f / sqrtf((float)DEC_D);
+
+    // Q^T fragments: lane (col, grp) holds q[head col][s*32 + grp*8 .. +8].
+    bf16x8 qf[4];
+    {
+        const __bf16* qr = q + ((int64_t)b * Hq + g * G + (col_ok ? col : 0)) * DEC_D + grp * 8;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint4 v = col_ok ? ld16(qr + s * 32) : make_uint4(0, 0, 0, 0);
+            qf[s] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    float mref = -INFINITY, lsum = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Prefetch registers: K fragments in A-operand order, V rows for the
+    // transposed LDS store (lane = 4 items of (key pair, 8-channel chunk)).
+    uint4 kreg[2][4];
+    uint4 vreg[4][2];
+    auto fetch = [&](int it) {
+        const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int key = kb + slot_key(col, t);
+            const bool ok = key < cend;
+            const __bf16* src = kc + (kv0 + (ok ? key : 0)) * DEC_D + grp * 8;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) kreg[t][s] = ok ? ld16(src + s * 32) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int item = lane + 64 * i;
+            const int kp = item >> 4, ch = item & 15;
+            const int key = kb + 2 * kp;
+            vreg[i][0] = key < cend ? ld16(vc + (kv0 + key) * DEC_D + ch * 8) : make_uint4(0, 0, 0, 0);
+            vreg[i][1] = key + 1 < cend ? ld16(vc + (kv0 + key + 1) * DEC_D + ch * 8)
+                                        : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    fetch(0);
+    for (int it = 0; it < DEC_ITERS; ++it) {
+        const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
+        const bool active = kb < cend;
+        // Only this wave touches its tile, and a wave's LDS operations complete
+        // in program order, so last iteration's reads precede these writes.
+        unsigned char* vt = lds + wave * DEC_VBYTES;
+        // V tile -> LDS, transposed to [channel][key].
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int item = lane + 64 * i;
+            const int kp = item >> 4, ch = item & 15;
+            const unsigned aw[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
+            const unsigned bw[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const unsigned lo = (e & 1) ? (aw[e >> 1] >> 16) : (aw[e >> 1] & 0xffffu);
+                const unsigned hi = (e & 1) ? (bw[e >> 1] & 0xffff0000u) : (bw[e >> 1] << 16);
+                *reinterpret_cast<unsigned*>(vt + (ch * 8 + e) * DEC_VROW + kp * 4) = lo | hi;
+            }
+        }
+        // S^T = K . Q^T for the two 16-key halves of the tile.
+        f32x4 s[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[t][st]),
+                                                               qf[st], s[t], 0, 0, 0);
+        }
+        if (it + 1 < DEC_ITERS) fetch(it + 1);
+        __syncthreads();
+        if (!active) continue;
+
+        // Mask positions past the chunk end; online softmax per head.
+        float sv[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = kb + slot_key(grp * 4 + r, t);
+                sv[t * 4 + r] = key < cend ? s[t][r] : -INFINITY;
+            }
+        float mx = sv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mref, mx);
+        const bool grow = mref == -INFINITY || (mnew - mref) * c > DEC_TAU;
+        if (__any(grow)) {
+            const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * c);  // 0 on first use
+            mref = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+        }
+        const float mc = mref * c;
+        bf16x8 pf;
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(sv[e], c, -mc)),
+                        __builtin_amdgcn_exp2f(fmaf(sv[e + 1], c, -mc))};
+            ls += pr[0] + pr[1];
+            bf16x2 pb = __builtin_convertvector(pr, bf16x2);
+            pf[e] = pb[0];
+            pf[e + 1] = pb[1];
+        }
+        lsum += ls;
+        // O^T += V^T . P^T over 8 blocks of 16 channels.
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            bf16x8 vf = __builtin_bit_cast(bf16x8, ld16(vt + (blk * 16 + col) * DEC_VROW + grp * 16));
+            acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[blk], 0, 0, 0);
+        }
+    }
+
+    // Every wave saw at least one key of the chunk only if its first tile was
+    // inside it; idle waves carry m = -inf, l = 0, O = 0 and merge as nothing.
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    __syncthreads();   // every wave is done reading its V^T tile
+    if (col_ok) {
+        if (grp == 0) {
+            merge_m[wave][col] = mref;
+            merge_l[wave][col] = lsum;
+        }
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) merge_o[wave][col][blk * 16 + grp * 4 + r] = acc[blk][r];
+    }
+    __syncthreads();
+    // Merge the waves: thread = (head, channel).
+    float* ws_split = ws + (((int64_t)b * Hq + g * G) * max_splits + split) * DEC_STATE;
+    for (int e = tid; e < G * DEC_D; e += DEC_THREADS) {
+        const int hh = e / DEC_D, ch = e % DEC_D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, merge_m[w][hh]);
+        float o = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w) {
+            const float mw = merge_m[w][hh];
+            const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mw - M) * c);
+            o = fmaf(merge_o[w][hh][ch], f, o);
+            l = fmaf(merge_l[w][hh], f, l);
+        }
+        float* st = ws_split + (int64_t)hh * max_splits * DEC_STATE;
+        st[ch] = o;
+        if (ch == 0) {
+            st[DEC_D] = M * c;
+            st[DEC_D + 1] = l;
+        }
+    }
+}
+
+// Merge the splits of both heads of a pair and combine them with lambda.
+__global__ void __launch_bounds__(DEC_D)
+decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict__ seq_lens, int Hq,
+                    int max_len, int max_splits, const float* __restrict__ lambda,
+                    float* __restrict__ out) {
+    const int p = blockIdx.x;
+    const int b = blockIdx.y;
+    const int ch = threadIdx.x;
+    const int P = Hq / 2;
+    const int L = seq_lens[b];
+    float* o = out + ((int64_t)b * P + p) * DEC_D;
+    if (L < 1 || L > max_len) {
+        o[ch] = 0.f;
+        return;
+    }
+    const int nsplit = (L + DEC_CHUNK - 1) / DEC_CHUNK;
+    float res[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const float* st = ws + ((int64_t)b * Hq + 2 * p + m) * max_splits * DEC_STATE;
+        float M = -INFINITY;
+        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, st[s * DEC_STATE + DEC_D]);
+        float acc = 0.f, l = 0.f;
+        for (int s = 0; s < nsplit; ++s) {
+            const float f = __builtin_amdgcn_exp2f(st[s * DEC_STATE + DEC_D] - M);
+            acc = fmaf(st[s * DEC_STATE + ch], f, acc);
+            l = fmaf(st[s * DEC_STATE + DEC_D + 1], f, l);
+        }
+        res[m] = acc / l;
+    }
+    o[ch] = res[0] - lambda[p] * res[1];
+}
+
+}  // namespace
+
+bool decode_supported(int D) { return D == DEC_D; }
+
+int decode_max_splits(int max_len) { return (max_len + DEC_CHUNK - 1) / DEC_CHUNK; }
+
+size_t decode_workspace_floats(int B, int Hq, int D, int max_len) {
+    (void)D;
+    return (size_t)B * Hq * decode_max_splits(max_len) * DEC_STATE;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+    if (a.D != DEC_D || a.Hq / a.Hkv > DEC_GROUP_MAX) return hipErrorInvalidValue;
+    const int S = decode_max_splits(a.max_len);
+    hipLaunchKernelGGL(decode_split_kernel, dim3(S, a.Hkv, a.B), dim3(DEC_THREADS), 0, stream,
+                       (const __bf16*)a.q, (const __bf16*)a.k_cache, (const __bf16*)a.v_cache,
+                       a.seq_lens, a.Hq, a.Hkv, a.max_len, S, a.workspace);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq / 2, a.B), dim3(DEC_D), 0, stream,
+                       a.workspace, a.seq_lens, a.Hq, a.max_len, S, a.lambda, a.out);
+    return hipGetLastError();
+}
+
+}  // namespace diffattn

@@ -1,0 +1,146 @@
+/*
+ * libdiffattn -- differential attention on AMD Instinct MI355X (gfx950).
+ *
+ * The operator (page "差分注意力" (aiknowledge.cn), part 一 "差分思路" and
+ * part 二 Step 2):
+ *     A1 = softmax(Q1 K1^T / sqrt(d)),   A2 = softmax(Q2 K2^T / sqrt(d)),
+ *     out = (A1 - lambda * A2) V,
+ * with d the length of the query/key dot product and lambda a per-head scalar
+ * (part 二 Step 4) whose initial value follows a depth schedule (page
+ * "【架构革新】Differential Transformer：用“差分降噪”重塑LLM注意力机制"
+ * (mcipr.com), section 3).  Two head layouts are served (page "差分注意力",
+ * "V1 到 V2 的 diff"): V1 splits each head's query and key into halves
+ * Q = (Q1, Q2), K = (K1, K2) over one value of full width and may normalise
+ * each head's output; V2 keeps full-width heads and doubles the query heads
+ * over the same KV heads.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (memory from hipMalloc or a
+ *    caller's allocator such as PyTorch).  The library allocates nothing,
+ *    keeps no state between calls, and never frees caller memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously; results are valid once the stream has
+ *    reached that point.  Calls on different streams may run concurrently;
+ *    every call only reads its inputs and writes its own outputs/workspace.
+ *  - Arguments are validated on the host before anything is enqueued.  On any
+ *    error no kernel is launched and no output is touched; the call returns a
+ *    status code and diffattn_last_error() (thread-local) describes it.
+ *  - Element strides are counted in elements of the tensor's own type.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef DIFFATTN_H_
+#define DIFFATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DIFFATTN_OK = 0,
+    DIFFATTN_ERR_INVALID_ARGUMENT = 1, /* null/host pointer, bad size, misalignment */
+    DIFFATTN_ERR_UNSUPPORTED = 2,      /* valid but not built: head width, dtype  */
+    DIFFATTN_ERR_WORKSPACE = 3,        /* workspace missing or too small          */
+    DIFFATTN_ERR_HIP = 4               /* the HIP runtime reported an error        */
+} diffattn_status_t;
+
+typedef enum {
+    DIFFATTN_FP32 = 0, /* fp32 inputs, fp32 arithmetic                           */
+    DIFFATTN_BF16 = 1  /* bf16 inputs, bf16 matrix products, fp32 accumulation   */
+} diffattn_dtype_t;
+
+/*
+ * lambda_init = 0.8 - 0.6 * exp(-0.3 * (layer - 1)), computed on the host in
+ * double.  `layer` is the 1-based layer index (page "【架构革新】...",
+ * section 3, initialisation strategy).  Returns NaN for layer < 1.
+ */
+double diffattn_lambda_init(int layer);
+
+/*
+ * Per-head lambda (page "差分注意力", part 二 Step 4 re-parameterisation):
+ *     lambda_h = exp(lq1_h . lk1_h) - exp(lq2_h . lk2_h) + lambda_init(layer).
+ * lq1, lk1, lq2, lk2: device fp32 [H][dim], row-major.
+ * lambda_out:         device fp32 [H].
+ * Each dot product is summed in double in index order, the exponentials and
+ * the sum are taken in double, and the result is rounded once to fp32.
+ * lambda may be negative or exceed 1; it is not clamped.
+ * Errors: INVALID_ARGUMENT for null or non-device pointers, H < 1, dim < 1,
+ * layer < 1.
+ */
+diffattn_status_t diffattn_lambda(const float* lq1, const float* lk1, const float* lq2,
+                                  const float* lk2, int H, int dim, int layer,
+                                  float* lambda_out, void* stream);
+
+/*
+ * Fused differential-attention prefill, V1 layout (page "差分注意力", part 一
+ * "差分思路" and "V1 到 V2 的 diff"; page "【架构革新】...", section 3: both
+ * softmaxes share their intermediates in one fused kernel).
+ *
+ * Tensors are [B][H][N][ld] (token-major inside each head): element (b,h,n,c)
+ * of q1 is q1[((b*H + h)*N + n)*ldq + c].  A packed [B][H][N][2d] query
+ * tensor is passed as q1 = base, q2 = base + d, ldq = 2d; the same for keys.
+ *   q1, q2, k1, k2 : d columns each (dtype), ldq/ldk >= d
+ *   v              : dv columns (dtype), ldv >= dv
+ *   lambda         : device fp32 [H] (e.g. from diffattn_lambda)
+ *   out            : device fp32 [B][H][N][dv], contiguous
+ * causal != 0: query n sees keys 0..n; otherwise all N keys.
+ * rmsnorm != 0: each output row of a head becomes
+ *     y_c = o_c / sqrt(mean_c o_c^2 + eps) * w_c * norm_scale,
+ * with w = norm_weight (device fp32 [dv]) or 1 if norm_weight is NULL; pass
+ * norm_scale = 1 - lambda_init for the V1 head normalisation.
+ * Supported: BF16 with (d, dv) in {(64,128), (64,64), (32,64), (128,128)};
+ * FP32 with d in {32, 64, 128} and dv in {64, 128}.  Other shapes return
+ * UNSUPPORTED.  Pointers must be 16-byte aligned and ld*sizeof(elem) a
+ * multiple of 16 (INVALID_ARGUMENT otherwise).  B, H, N >= 1.
+ */
+diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k1,
+                                   const void* k2, const void* v, int64_t ldq, int64_t ldk,
+                                   int64_t ldv, diffattn_dtype_t dtype, int B, int H, int N,
+                                   int d, int dv, int causal, const float* lambda, int rmsnorm,
+                                   float eps, float norm_scale, const float* norm_weight,
+                                   float* out, void* stream);
+
+/*
+ * Bytes of device workspace diffattn_decode needs for these sizes (partial
+ * softmax states of every KV split).  Returns 0 for invalid sizes.
+ */
+size_t diffattn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len);
+
+/*
+ * One-token differential-attention decode over a KV cache, V2 layout (page
+ * "差分注意力", "V1 到 V2 的 diff": twice the query heads over unchanged KV
+ * heads, so one pass over the cache serves both maps; part 五 exercise 3 on
+ * decode arithmetic intensity).
+ *   q        : device bf16 [B][Hq][D]
+ *   k_cache,
+ *   v_cache  : device bf16 [B][Hkv][max_len][D]; positions 0..L_b-1 are read
+ *   seq_lens : device int32 [B], 1 <= L_b <= max_len
+ *   lambda   : device fp32 [Hq/2], one per pair
+ *   out      : device fp32 [B][Hq/2][D]
+ * Pair p takes query head 2p for A1 and 2p+1 for A2, both over KV head
+ * floor(2p / (Hq/Hkv)); Hq must be a multiple of 2*Hkv.  There is no output
+ * normalisation in this layout.
+ * workspace: device memory of at least diffattn_decode_workspace_bytes(...)
+ * bytes, 256-byte aligned, owned by the caller, overwritten by the call.
+ * Supported: D = 128.  A sequence whose device-side length lies outside
+ * [1, max_len] (the host cannot see it) yields zeros for its outputs.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (D), WORKSPACE (missing/too small).
+ */
+diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                  int max_len, const float* lambda, void* workspace,
+                                  size_t workspace_bytes, float* out, void* stream);
+
+/* Static text for a status code. */
+const char* diffattn_status_string(diffattn_status_t status);
+
+/* Detail of the last error reported on the calling thread ("" if none). */
+const char* diffattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H_ */

@@ -1,0 +1,129 @@
+"""The C-ABI library: it loads, exports every declared entry point, and its
+host-side validation returns the documented status codes.  CPU only: every
+call here is rejected before the HIP runtime is touched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from differential_attention_prefill_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "diffattn.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+FAKE = 0x10000          # non-null, 256-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.LIB_PATH):
+        from differential_attention_prefill_amd import build
+        build.build()
+    return api.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(api.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_lambda_init_host_values(lib):
+    assert abs(api.diffattn_lambda_init(1) - 0.2) < 1e-15
+    assert abs(api.diffattn_lambda_init(6) - (0.8 - 0.6 * 2.718281828459045 ** -1.5)) < 1e-15
+    assert api.diffattn_lambda_init(0) != api.diffattn_lambda_init(0)   # NaN
+
+
+def test_lambda_init_matches_oracle(lib, oracle_mod):
+    for layer in range(1, 40):
+        assert api.diffattn_lambda_init(layer) == oracle_mod.lambda_init(layer)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.diffattn_status_string(code)
+
+
+def _prefill(lib, **kw):
+    a = dict(q1=FAKE, q2=FAKE, k1=FAKE, k2=FAKE, v=FAKE, ldq=128, ldk=128, ldv=128, dtype=1,
+             B=1, H=2, N=16, d=64, dv=128, causal=1, lam=FAKE, rmsnorm=0, eps=1e-5,
+             norm_scale=1.0, norm_weight=None, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.diffattn_prefill(a["q1"], a["q2"], a["k1"], a["k2"], a["v"], a["ldq"], a["ldk"],
+                                a["ldv"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["dv"],
+                                a["causal"], a["lam"], a["rmsnorm"], a["eps"], a["norm_scale"],
+                                a["norm_weight"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q1=None), INVALID), (dict(v=None), INVALID), (dict(lam=None), INVALID),
+    (dict(out=None), INVALID), (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(H=-1), INVALID),
+    (dict(dtype=7), INVALID), (dict(ldq=32), INVALID), (dict(ldv=100), INVALID),
+    (dict(ldk=68), INVALID), (dict(q2=FAKE + 2), INVALID), (dict(out=FAKE + 4), INVALID),
+    (dict(lam=FAKE + 2), INVALID), (dict(rmsnorm=1, eps=-1.0), INVALID),
+    (dict(d=48), UNSUPPORTED), (dict(dv=96, ldv=96), UNSUPPORTED),
+    (dict(dtype=0, d=16, ldq=64, ldk=64), UNSUPPORTED),
+])
+def test_prefill_validation(lib, kw, code):
+    assert _prefill(lib, **kw) == code
+    assert lib.diffattn_last_error().decode()
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, B=2, Hq=8, Hkv=2, D=128, max_len=4096,
+             lam=FAKE, ws=FAKE, ws_bytes=1 << 30, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.diffattn_decode(a["q"], a["k"], a["v"], a["lens"], a["B"], a["Hq"], a["Hkv"],
+                               a["D"], a["max_len"], a["lam"], a["ws"], a["ws_bytes"], a["out"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(lens=None), INVALID), (dict(B=0), INVALID),
+    (dict(Hq=6), INVALID), (dict(Hkv=3), INVALID), (dict(max_len=0), INVALID),
+    (dict(k=FAKE + 8), INVALID), (dict(lens=FAKE + 2), INVALID), (dict(ws=FAKE + 16), INVALID),
+    (dict(D=64), UNSUPPORTED), (dict(Hq=64, Hkv=2), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+])
+def test_decode_validation(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_workspace_size(lib):
+    n = api.diffattn_decode_workspace_bytes(32, 32, 8, 128, 65536)
+    assert n >= 32 * 32 * 130 * 4 and n % 4 == 0
+    assert api.diffattn_decode_workspace_bytes(0, 32, 8, 128, 65536) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(lq1=None), dict(H=0), dict(dim=0), dict(layer=0)])
+def test_lambda_validation(lib, kw):
+    a = dict(lq1=FAKE, lk1=FAKE, lq2=FAKE, lk2=FAKE, H=4, dim=32, layer=1, out=FAKE)
+    a.update(kw)
+    assert lib.diffattn_lambda(a["lq1"], a["lk1"], a["lq2"], a["lk2"], a["H"], a["dim"],
+                               a["layer"], a["out"], None) == INVALID
+
+
+def test_no_oracle_in_product_path():
+    # The product sources never reference the oracle.
+    pkg = os.path.join(ROOT, "differential_attention_prefill_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "liboracle" not in text, f

@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs, element by element, plus invariants that hold at any
+size.  Every test prints its case before touching the GPU."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differential_attention_prefill_amd import api
+from differential_attention_prefill_amd import workloads as W
+
+from parity_util import (compare, gpu_lambda, run_prefill_gpu, run_prefill_oracle, say)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.load_library()
+
+
+# ---------------------------------------------------------------------------
+# lambda: bit-identical in fp32
+# ---------------------------------------------------------------------------
+
+def assert_lambda_bitwise(inp, layer, lam_gpu):
+    want = oracle.compute_lambda(inp["lq1"].cpu(), inp["lk1"].cpu(), inp["lq2"].cpu(),
+                                 inp["lk2"].cpu(), layer)
+    got = lam_gpu.cpu().numpy()
+    assert got.view(np.uint32).tolist() == want.view(np.uint32).tolist()
+
+
+def test_lambda_bitwise_many_heads_and_layers():
+    g = torch.Generator().manual_seed(99)
+    for layer in (1, 2, 6, 12, 24):
+        for dim in (1, 7, 32, 64, 128, 1000):
+            lq = [torch.randn((64, dim), generator=g) * 0.1 for _ in range(4)]
+            say("lambda layer=%d dim=%d" % (layer, dim))
+            want = oracle.compute_lambda(*lq, layer)
+            got = api.diffattn_lambda(*(t.to(DEV) for t in lq), layer=layer).cpu().numpy()
+            assert got.view(np.uint32).tolist() == want.view(np.uint32).tolist()
+
+
+# ---------------------------------------------------------------------------
+# fp32 prefill
+# ---------------------------------------------------------------------------
+
+def _prefill_case_check(case, rows=None, **over):
+    inp = W.make_prefill(case, device=DEV)
+    lam_gpu = gpu_lambda(inp, case.layer)
+    assert_lambda_bitwise(inp, case.layer, lam_gpu)
+    lam = lam_gpu.cpu().numpy()
+    out = run_prefill_gpu(case, inp, lam_gpu, **over)
+    torch.cuda.synchronize()
+    ref = run_prefill_oracle(case, inp, lam, rows=rows, **over)
+    got = out.cpu().numpy()
+    if rows is not None:
+        got = got.reshape(-1, case.dv)[rows]
+    return compare(got, ref, case.dtype, case.name)
+
+
+def test_prefill_fp32_tiny_workload():
+    say("fp32 prefill %s" % W.TINY_FP32.name)
+    _prefill_case_check(W.TINY_FP32)
+
+
+@pytest.mark.parametrize("d,dv,N,causal,rms", [
+    (32, 64, 1, True, False), (32, 64, 77, True, True), (64, 128, 100, False, False),
+    (64, 64, 33, True, True), (128, 128, 50, True, False), (128, 64, 65, False, True),
+    (32, 128, 129, True, False),
+])
+def test_prefill_fp32_shapes(d, dv, N, causal, rms):
+    case = W.PrefillCase("fp32_d%d_dv%d_n%d" % (d, dv, N), "fp32", B=2, H=3, N=N, d=d, dv=dv,
+                         layer=3, rmsnorm=rms, seed=1000 + N, causal=causal)
+    say("fp32 prefill %s causal=%s rms=%s" % (case.name, causal, rms))
+    _prefill_case_check(case)
+
+
+# ---------------------------------------------------------------------------
+# bf16 prefill (the fused MFMA kernel)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,dv,N,causal,rms", [
+    (64, 128, 1, True, False), (64, 128, 31, True, True), (64, 128, 32, True, False),
+    (64, 128, 33, True, False), (64, 128, 300, True, True), (64, 128, 517, False, False),
+    (64, 128, 257, False, True), (64, 64, 200, True, True), (32, 64, 160, True, False),
+    (128, 128, 190, True, False), (128, 128, 64, False, True),
+])
+def test_prefill_bf16_shapes(d, dv, N, causal, rms):
+    case = W.PrefillCase("bf16_d%d_dv%d_n%d" % (d, dv, N), "bf16", B=2, H=3, N=N, d=d, dv=dv,
+                         layer=4, rmsnorm=rms, seed=2000 + N, causal=causal)
+    say("bf16 prefill %s causal=%s rms=%s" % (case.name, causal, rms))
+    _prefill_case_check(case)
+
+
+def test_prefill_bf16_norm_weight():
+    case = W.PrefillCase("bf16_weighted_norm", "bf16", B=1, H=2, N=130, d=64, dv=128, layer=6,
+                         rmsnorm=True, seed=77)
+    w = (1.0 + 0.5 * torch.randn(128, generator=torch.Generator().manual_seed(5))).float()
+    say("bf16 prefill with a norm weight")
+    inp = W.make_prefill(case, device=DEV)
+    lam_gpu = gpu_lambda(inp, case.layer)
+    out = run_prefill_gpu(case, inp, lam_gpu, norm_weight=w.to(DEV)).cpu().numpy()
+    ref = run_prefill_oracle(case, inp, lam_gpu.cpu().numpy(), norm_weight=w)
+    compare(out, ref, "bf16", case.name)
+
+
+def test_prefill_v1_norm_workload_full():
+    # B=4, H=16, N=2048, d=64, dv=128, RMS norm x (1 - lambda_init(6)): every row.
+    say("bf16 prefill %s (all rows)" % W.V1_NORM.name)
+    _prefill_case_check(W.V1_NORM)
+
+
+def _sample_rows(case, needles, per_head=24, seed=0):
+    """Rows to check at full size: first/last rows, needle rows, random rows."""
+    g = np.random.default_rng(seed)
+    rows = []
+    for b in range(case.B):
+        for h in range(case.H):
+            base = (b * case.H + h) * case.N
+            pick = set([0, 1, 31, 32, 127, 128, case.N - 1, case.N - 2, case.N - 33])
+            for p in np.asarray(needles[h]).reshape(-1)[:4]:
+                pick.update([int(p), min(case.N - 1, int(p) + 1)])
+            pick.update(g.integers(0, case.N, size=per_head).tolist())
+            rows.extend(base + r for r in sorted(pick) if 0 <= r < case.N)
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("case", [W.NEEDLE_32K, W.MULTI_NEEDLE_64K], ids=lambda c: c.name)
+def test_prefill_long_workloads_sampled(case):
+    say("bf16 prefill %s (sampled rows, full size)" % case.name)
+    inp = W.make_prefill(case, device=DEV)
+    rows = _sample_rows(case, inp["needles"])
+    lam_gpu = gpu_lambda(inp, case.layer)
+    assert_lambda_bitwise(inp, case.layer, lam_gpu)
+    out = run_prefill_gpu(case, inp, lam_gpu)
+    torch.cuda.synchronize()
+    got = out.reshape(-1, case.dv)[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    del out
+    ref = run_prefill_oracle(case, inp, lam_gpu.cpu().numpy(), rows=rows)
+    compare(got, ref, "bf16", case.name + " sampled")
+
+
+# ---------------------------------------------------------------------------
+# bf16 prefill invariants
+# ---------------------------------------------------------------------------
+
+def _rand_bf16(shape, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16)
+
+
+def test_prefill_rows_sum_to_one_minus_lambda():
+    # A value tensor of ones reads off the row sums of A1 - lam A2 = 1 - lam.
+    B, H, N, d, dv = 1, 4, 700, 64, 128
+    say("bf16 row-sum invariant N=%d" % N)
+    q, k = _rand_bf16((B, H, N, 2 * d), 1), _rand_bf16((B, H, N, 2 * d), 2)
+    v = torch.ones((B, H, N, dv), dtype=torch.bfloat16, device=DEV)
+    lam = torch.tensor([0.2, 0.8, -0.5, 1.3], device=DEV)
+    out = api.diffattn_prefill_packed(q, k, v, lam).cpu().double()
+    want = (1 - lam.cpu().double()).view(1, H, 1, 1).expand_as(out)
+    assert (out - want).abs().max().item() < 1e-2
+
+
+def test_prefill_identical_maps_cancel():
+    B, H, N, d, dv = 2, 2, 333, 64, 128
+    say("bf16 identical maps with lambda=1")
+    qh, kh = _rand_bf16((B, H, N, d), 3), _rand_bf16((B, H, N, d), 4)
+    v = _rand_bf16((B, H, N, dv), 5)
+    lam = torch.ones(H, device=DEV)
+    out = api.diffattn_prefill(qh, qh, kh, kh, v, lam)
+    assert out.abs().max().item() <= 1e-6
+
+
+def test_prefill_causality_and_determinism():
+    B, H, N, d, dv = 1, 2, 400, 64, 128
+    say("bf16 causality / determinism")
+    q, k, v = _rand_bf16((B, H, N, 2 * d), 6), _rand_bf16((B, H, N, 2 * d), 7), _rand_bf16((B, H, N, dv), 8)
+    lam = torch.tensor([0.3, 0.6], device=DEV)
+    a = api.diffattn_prefill_packed(q, k, v, lam)
+    b = api.diffattn_prefill_packed(q, k, v, lam)
+    assert torch.equal(a, b)
+    i = 170
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, i + 1:] = _rand_bf16((B, H, N - i - 1, 2 * d), 9)
+    v2[:, :, i + 1:] = _rand_bf16((B, H, N - i - 1, dv), 10)
+    c = api.diffattn_prefill_packed(q, k2, v2, lam)
+    assert torch.equal(a[:, :, : i + 1], c[:, :, : i + 1])
+    assert not torch.equal(a[:, :, i + 1:], c[:, :, i + 1:])
+
+
+def test_prefill_separate_tensors_match_packed():
+    B, H, N, d, dv = 1, 2, 96, 64, 128
+    say("bf16 separate Q1/Q2/K1/K2 tensors")
+    q, k, v = _rand_bf16((B, H, N, 2 * d), 11), _rand_bf16((B, H, N, 2 * d), 12), _rand_bf16((B, H, N, dv), 13)
+    lam = torch.tensor([0.4, 0.1], device=DEV)
+    a = api.diffattn_prefill_packed(q, k, v, lam)
+    b = api.diffattn_prefill(q[..., :d].contiguous(), q[..., d:].contiguous(),
+                             k[..., :d].contiguous(), k[..., d:].contiguous(), v, lam)
+    assert torch.equal(a, b)
+
+
+def test_prefill_rejects_host_pointer():
+    lib = api.load_library()
+    host = torch.zeros((1, 1, 16, 128), dtype=torch.bfloat16)
+    dev = torch.zeros((1, 1, 16, 128), dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros((1, 1, 16, 128), device=DEV)
+    lam = torch.zeros(1, device=DEV)
+    st = lib.diffattn_prefill(host.data_ptr(), dev.data_ptr() + 128, dev.data_ptr(),
+                              dev.data_ptr() + 128, dev.data_ptr(), 128, 128, 128, 1, 1, 1, 16,
+                              64, 128, 1, lam.data_ptr(), 0, 1e-5, 1.0, None, out.data_ptr(), None)
+    assert st == 1
+    assert torch.count_nonzero(out).item() == 0
+
+
+# ---------------------------------------------------------------------------
+# decode (V2 layout)
+# ---------------------------------------------------------------------------
+
+def _decode_check(case, fill_unused=None):
+    inp = W.make_decode(case, device=DEV, fill_unused=fill_unused)
+    lam_gpu = gpu_lambda(inp, case.layer)
+    assert_lambda_bitwise(inp, case.layer, lam_gpu)
+    out = api.diffattn_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam_gpu)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = oracle.decode(inp["q"].cpu(), inp["k_cache"].cpu(), inp["v_cache"].cpu(),
+                        inp["seq_lens"].cpu(), lam_gpu.cpu().numpy())
+    return compare(got, ref, "bf16", case.name)
+
+
+@pytest.mark.parametrize("lens", [[1, 2, 31, 33], [1023, 1024, 1025, 3000], [4096, 777, 4095, 64]])
+def test_decode_ragged_lengths(lens):
+    case = W.DecodeCase("decode_small_%d" % lens[0], B=len(lens), Hq=8, Hkv=2, D=128,
+                        Lmin=1, Lmax=max(lens), layer=2, seed=sum(lens))
+    say("decode lens=%s" % lens)
+    inp = W.make_decode(case, device=DEV)
+    inp["seq_lens"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    for b, L in enumerate(lens):   # unused cache slots hold NaN: they must not be read
+        inp["k_cache"][b, :, L:] = float("nan")
+        inp["v_cache"][b, :, L:] = float("nan")
+    lam_gpu = gpu_lambda(inp, case.layer)
+    out = api.diffattn_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam_gpu)
+    ref = oracle.decode(inp["q"].cpu(), inp["k_cache"].cpu(), inp["v_cache"].cpu(),
+                        inp["seq_lens"].cpu(), lam_gpu.cpu().numpy())
+    compare(out.cpu().numpy(), ref, "bf16", case.name)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (16, 2), (32, 8), (8, 4)])
+def test_decode_group_sizes(hq, hkv):
+    case = W.DecodeCase("decode_g%d" % (hq // hkv), B=2, Hq=hq, Hkv=hkv, D=128, Lmin=500,
+                        Lmax=2500, layer=1, seed=hq * 10 + hkv)
+    say("decode Hq=%d Hkv=%d" % (hq, hkv))
+    _decode_check(case, fill_unused=float("nan"))
+
+
+def test_decode_invalid_device_length_gives_zeros():
+    case = W.DecodeCase("decode_badlen", B=3, Hq=8, Hkv=2, D=128, Lmin=10, Lmax=300, layer=1,
+                        seed=5)
+    say("decode with an out-of-range device length")
+    inp = W.make_decode(case, device=DEV)
+    inp["seq_lens"] = torch.tensor([100, 0, 301], dtype=torch.int32, device=DEV)
+    lam = gpu_lambda(inp, 1)
+    out = api.diffattn_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam)
+    assert torch.count_nonzero(out[1:]).item() == 0
+    ref = oracle.decode(inp["q"][:1].cpu(), inp["k_cache"][:1].cpu(), inp["v_cache"][:1].cpu(),
+                        np.array([100], np.int32), lam.cpu().numpy())
+    compare(out[:1].cpu().numpy(), ref, "bf16", "decode valid row")
+
+
+def test_decode_v2_workload_full():
+    # B=32, Hq=32 (16 pairs), Hkv=8, D=128, lengths uniform in [4096, 65536].
+    say("decode %s (all outputs)" % W.V2_DECODE.name)
+    _decode_check(W.V2_DECODE)
