@@ -58,6 +58,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, copy this many MiB device-to-device once: "
+                         "a plain copy of known size that calibrates HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -182,6 +185,16 @@ def main():
         },
         "lambda_avg_ms": round(float(np.mean(t_lam)), 4),
     }
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = n
+        del src, dst
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pcase, pin, dcase, din, plam, dlam, norm_scale,
