@@ -243,36 +243,59 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
 }
 
 // Merge the splits of both heads of a pair and combine them with lambda.
-__global__ void __launch_bounds__(DEC_D)
+// 256 threads: thread (m, ch) owns channel ch of head 2p+m.  The split maxima
+// are reduced once through LDS; each thread then sums its channel over the
+// splits with independent loads (unrolled), so the kernel is not a chain of
+// dependent global reads.
+constexpr int MERGE_THREADS = 2 * DEC_D;
+constexpr int MERGE_LDS_SPLITS = 1024;   // splits whose weights are cached in LDS
+
+__global__ void __launch_bounds__(MERGE_THREADS)
 decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict__ seq_lens, int Hq,
                     int max_len, int max_splits, const float* __restrict__ lambda,
                     float* __restrict__ out) {
     const int p = blockIdx.x;
     const int b = blockIdx.y;
-    const int ch = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int m = tid / DEC_D;        // 0: head 2p (A1), 1: head 2p+1 (A2)
+    const int ch = tid % DEC_D;
     const int P = Hq / 2;
     const int L = seq_lens[b];
     float* o = out + ((int64_t)b * P + p) * DEC_D;
-    if (L < 1 || L > max_len) {
-        o[ch] = 0.f;
+    if (L < 1 || L > max_len) {       // block-uniform
+        if (tid < DEC_D) o[tid] = 0.f;
         return;
     }
     const int nsplit = (L + DEC_CHUNK - 1) / DEC_CHUNK;
-    float res[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const float* st = ws + ((int64_t)b * Hq + 2 * p + m) * max_splits * DEC_STATE;
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, st[s * DEC_STATE + DEC_D]);
-        float acc = 0.f, l = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float f = __builtin_amdgcn_exp2f(st[s * DEC_STATE + DEC_D] - M);
-            acc = fmaf(st[s * DEC_STATE + ch], f, acc);
-            l = fmaf(st[s * DEC_STATE + DEC_D + 1], f, l);
-        }
-        res[m] = acc / l;
+    __shared__ float w_lds[2][MERGE_LDS_SPLITS];
+    __shared__ float red[2][MERGE_THREADS / 64];
+    __shared__ float res[DEC_D];
+    const float* st = ws + ((int64_t)b * Hq + 2 * p + m) * max_splits * DEC_STATE;
+
+    // Maximum of the split maxima of this thread's head (both heads at once:
+    // threads 0..127 scan head 0, 128..255 head 1).
+    float M = -INFINITY;
+    for (int s = ch; s < nsplit; s += DEC_D) M = fmaxf(M, st[(int64_t)s * DEC_STATE + DEC_D]);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if ((tid & 63) == 0) red[m][(tid % DEC_D) / 64] = M;
+    __syncthreads();
+    M = fmaxf(red[m][0], red[m][1]);
+    // Split weights 2^(m_s - M), cached for the first MERGE_LDS_SPLITS splits.
+    for (int s = ch; s < min(nsplit, MERGE_LDS_SPLITS); s += DEC_D)
+        w_lds[m][s] = __builtin_amdgcn_exp2f(st[(int64_t)s * DEC_STATE + DEC_D] - M);
+    __syncthreads();
+    float acc = 0.f, l = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) {
+        const float f = s < MERGE_LDS_SPLITS ? w_lds[m][s]
+                                             : __builtin_amdgcn_exp2f(st[(int64_t)s * DEC_STATE + DEC_D] - M);
+        acc = fmaf(st[(int64_t)s * DEC_STATE + ch], f, acc);
+        l = fmaf(st[(int64_t)s * DEC_STATE + DEC_D + 1], f, l);
     }
-    o[ch] = res[0] - lambda[p] * res[1];
+    const float r = acc / l;
+    if (m == 1) res[ch] = r;
+    __syncthreads();
+    if (m == 0) o[ch] = r - lambda[p] * res[ch];
 }
 
 }  // namespace
@@ -294,7 +317,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
                        a.seq_lens, a.Hq, a.Hkv, a.max_len, S, a.workspace);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq / 2, a.B), dim3(DEC_D), 0, stream,
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq / 2, a.B), dim3(MERGE_THREADS), 0, stream,
                        a.workspace, a.seq_lens, a.Hq, a.max_len, S, a.lambda, a.out);
     return hipGetLastError();
 }

@@ -10,11 +10,13 @@
 // One pass over a shared key/value stream (page "【架构革新】...", section 3:
 // the two softmaxes share intermediates inside one fused kernel):
 //  - A workgroup owns BM = 32*WAVES query rows of one head; each wave owns 32
-//    rows.  Keys and values stream through LDS in tiles of 32 keys, double
-//    buffered: the next tile's global loads are issued before the current
-//    tile is computed.  Keys hold both halves K1|K2 in one LDS row; values
-//    stay token-major, and the P.V product, which contracts over keys, reads
-//    its V^T operand with the gfx950 LDS transpose load (ds_read_b64_tr_b16):
+//    rows.  Keys and values stream through LDS in tiles of 64 keys, double
+//    buffered, copied by buffer loads that write LDS directly (no staging
+//    registers); the copy of tile T+1 runs while tile T is computed, and
+//    one barrier per tile hands a stage over.  Rows are XOR-swizzled in
+//    16-byte chunks so that fragment reads hit distinct banks.  Values stay
+//    token-major, and the P.V product, which contracts over keys, reads its
+//    V^T operand with the gfx950 LDS transpose load (ds_read_b64_tr_b16):
 //    each 16-lane group reads a 4-key x 16-channel block and every lane
 //    receives 4 keys of one channel.
 //  - Two workgroups share a CU (<= 256 registers per lane), so one wave's
@@ -59,22 +61,41 @@ template <int D, int DV, int WAVES>
 struct Cfg {
     static constexpr int THREADS = WAVE * WAVES;
     static constexpr int BM = QROWS * WAVES;
-    // Row pitches in LDS.  A key row (K1|K2) is padded by 16 bytes so that
-    // the 16 rows read by one 16-lane quarter land in distinct banks; a value
-    // row is padded so consecutive rows start 16 banks apart, which keeps the
-    // 4-row x 32-byte blocks of the transpose load conflict-free.
-    static constexpr int KROW = 2 * D * 2 + 16;
-    static constexpr int VROW = DV * 2 + 64;
-    static constexpr int KBYTES = BN * KROW;
-    static constexpr int VBYTES = BN * VROW;
-    static constexpr int STAGE = KBYTES + VBYTES;
-    static constexpr int KCHUNKS = BN * (2 * D) / 8;   // 16-byte chunks per key tile
-    static constexpr int KPT = (KCHUNKS + THREADS - 1) / THREADS;
-    static constexpr int VCHUNKS = BN * DV / 8;        // 16-byte chunks per value tile
-    static constexpr int VPT = (VCHUNKS + THREADS - 1) / THREADS;
-    static constexpr int KSTEPS = D / 16;             // MFMA k-steps for one score map
-    static constexpr int VBLK = DV / 32;              // 32-channel blocks of O^T
+    static constexpr int TK = 2 * BN;                 // keys per stage (two 32-key sub-tiles)
+    static constexpr int KC = D / 8;                  // 16-byte chunks per key half-row
+    static constexpr int VC = DV / 8;                 // 16-byte chunks per value row
+    static constexpr int KROWB = D * 2;               // bytes per key half-row (K1 or K2)
+    static constexpr int VROWB = DV * 2;              // bytes per value row
+    static constexpr int K1_OFF = 0;
+    static constexpr int K2_OFF = TK * KROWB;
+    static constexpr int V_OFF = 2 * TK * KROWB;
+    static constexpr int STAGE = 2 * TK * KROWB + TK * VROWB;
+    // One LDS-DMA instruction moves 1 KB (64 lanes x 16 bytes).
+    static constexpr int KI = TK * KROWB / 1024 / WAVES;   // per wave, per key half
+    static constexpr int VI = TK * VROWB / 1024 / WAVES;   // per wave
+    static constexpr int KRPI = 1024 / KROWB;              // key rows per DMA instruction
+    static constexpr int VRPI = 1024 / VROWB;              // value rows per DMA instruction
+    static constexpr int KSTEPS = D / 16;                  // MFMA k-steps for one score map
+    static constexpr int VBLK = DV / 32;                   // 32-channel blocks of O^T
+    static_assert(KI >= 1 && VI >= 1, "tile must give every wave whole DMA instructions");
 };
+
+// Chunk swizzles (physical chunk = logical chunk ^ swizzle(row)).
+// Keys: the 16 rows read by one 16-lane quarter must land in 16 distinct
+// 16-byte bank groups of a 256-byte bank line.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+    constexpr int KC = D / 8, RPB = 256 / (D * 2);     // rows per 256-byte bank line
+    return (row / RPB) % KC;
+}
+// Values: a transpose load reads 4 consecutive rows x 32 bytes per 16-lane
+// group; the swizzle spreads them (and the neighbouring group's) over
+// distinct bank groups.
+template <int DV>
+__device__ __forceinline__ int v_swz(int row) {
+    if constexpr (DV == 128) return 4 * (row & 3);
+    else return 2 * ((row >> 1) & 1);
+}
 
 // Row slot rho of the S^T tile holds key kappa(rho): bits 2 and 3 swapped.
 __device__ __forceinline__ int kappa(int rho) {
@@ -85,12 +106,12 @@ __device__ __forceinline__ uint4 load16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
-// max(a, b, c) in one instruction.  Written out because fmaxf chains get an
-// extra quieting max per operand in IEEE mode; scores are never NaN here.
+// max(a, b, c): this file is compiled with IEEE mode off and NaNs not
+// honoured, so the chain lowers to one v_max3_f32 with no quieting of its
+// inputs.  (It must stay visible to the compiler: reading matrix-core
+// results needs wait states that only the compiler inserts.)
 __device__ __forceinline__ float max3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return fmaxf(fmaxf(a, b), c);
 }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -108,6 +129,35 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
 // OCC: waves per SIMD the register budget is cut for (2 lets one wave's
 // softmax overlap the other's matrix products; d = 128 keeps 1 so that its
 // larger query fragments stay in registers).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (gfx9-family layout): base, stride 0, byte extent.
+// Loads at offsets >= `bytes` return zeros.  Scalar registers throughout.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+    const unsigned long long a = (unsigned long long)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(size_t)((__attribute__((address_space(3))) const unsigned char*)p);
+}
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds_base + 16*lane (lds_base wave-uniform).  Written as an instruction the
+// compiler does not track: it would otherwise wait for every copy in flight
+// before each LDS read.  Completion is awaited explicitly (vmcnt) before the
+// barrier that publishes a stage.
+__device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, unsigned lds_base, int voff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
+}
+
 template <int D, int DV, int WAVES, int OCC>
 __global__ void __launch_bounds__(WAVE * WAVES) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
@@ -122,7 +172,9 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // Wave-uniform values live in scalar registers, so tile skipping and
+    // masking decisions are scalar branches rather than per-lane selects.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;   // query column inside the wave's 32 rows
     const int half = lane >> 5;  // which 8-element half of each 16-element k-step
 
@@ -169,77 +221,74 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
             for (int r = 0; r < 16; ++r) acc[m][nb][r] = 0.f;
 
     const int kv_end = causal ? min(N, q0 + C::BM) : N;
-    const int ntiles = (kv_end + BN - 1) / BN;
 
-    // Lane-constant LDS offsets.
-    // K fragment: row kappa(col), 8 elements at half*8 of each k-step.
-    const int k_lane_off = kappa(col) * C::KROW + half * 16;
+    // Lane-constant LDS offsets (within a stage, sub-tile 0; sub-tile 1 adds
+    // 32 rows, which leaves both swizzles unchanged).
+    // K fragment of k-step st: row kappa(col), logical chunk 2*st + half.
+    int k_frag[C::KSTEPS];
+    {
+        const int row = kappa(col);
+#pragma unroll
+        for (int st = 0; st < C::KSTEPS; ++st)
+            k_frag[st] = row * C::KROWB + (((2 * st + half) ^ k_swz<D>(row)) * 16);
+    }
     // V^T fragment through the transpose load: group g = lane/16 covers
     // channels 16*(g%2) .. +15 of a 32-channel block and keys 8*(g/2) .. +7 of
     // a 16-key step; lane j of the group points at key 4*r + j/4, channels
     // 4*(j%4) .. +3 for the two loads r = 0, 1.
     const int grp = lane >> 4, gl = lane & 15;
-    const int v_lane_off = ((grp >> 1) * 8 + (gl >> 2)) * C::VROW + (16 * (grp & 1) + 4 * (gl & 3)) * 2;
+    int v_frag[C::VBLK];
+    {
+        const int row = (grp >> 1) * 8 + (gl >> 2);          // + t2*16 + r*4 (+32 per sub-tile)
+#pragma unroll
+        for (int nb = 0; nb < C::VBLK; ++nb) {
+            const int chunk = nb * 4 + 2 * (grp & 1) + ((gl & 3) >> 1);
+            v_frag[nb] = C::V_OFF + row * C::VROWB + ((chunk ^ v_swz<DV>(row)) * 16) + 8 * (gl & 1);
+        }
+    }
 
-    // ---- global -> register prefetch of one key/value tile --------------
-    uint4 kreg[C::KPT];
-    uint4 vreg[C::VPT];
-    auto fetch = [&](int t) {
-        const int kb = t * BN;
-        // Positions past the sequence end load row 0 of the head instead:
-        // their scores are masked to -inf, so their probabilities are exactly
-        // zero and the row contributes nothing.  (Selecting zeros here would
-        // make every load wait for its data immediately.)
-#pragma unroll
-        for (int i = 0; i < C::KPT; ++i) {
-            const int ch = tid + i * C::THREADS;
-            const int key = ch / (D / 4);
-            const int part = ch % (D / 4);           // 16-byte chunk of K1|K2
-            const bool ok = (C::KCHUNKS % C::THREADS == 0 || ch < C::KCHUNKS) && kb + key < N;
-            const int64_t row = tok0 + (ok ? kb + key : 0);
-            kreg[i] = load16((part < D / 8) ? k1 + row * ldk + part * 8
-                                            : k2 + row * ldk + (part - D / 8) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < C::VPT; ++i) {
-            const int ch = tid + i * C::THREADS;
-            const int key = ch / (DV / 8);
-            const int part = ch % (DV / 8);
-            const bool ok = (C::VCHUNKS % C::THREADS == 0 || ch < C::VCHUNKS) && kb + key < N;
-            vreg[i] = load16(v + (tok0 + (ok ? kb + key : 0)) * ldv + part * 8);
-        }
+    // ---- global -> LDS copies of one 64-key tile ------------------------
+    // Buffer descriptors start at the tile's first key and end at the
+    // sequence end: rows past N read as zeros (their scores are masked).
+    auto rsrc = [&](const __bf16* base, int64_t ld, int kb) {
+        const int rows = max(0, min(N - kb, C::TK));
+        return make_rsrc(base + (tok0 + kb) * ld, rows * (int)ld * 2);
     };
-    auto stash = [&](int stage) {
-        unsigned char* base = smem + stage * C::STAGE;
+    // Lane-constant source offsets of this wave's DMA instructions.
+    int koff[C::KI], voff[C::VI];
 #pragma unroll
-        for (int i = 0; i < C::KPT; ++i) {
-            const int ch = tid + i * C::THREADS;
-            if (ch < C::KCHUNKS)
-                *reinterpret_cast<uint4*>(base + (ch / (D / 4)) * C::KROW + (ch % (D / 4)) * 16) = kreg[i];
+    for (int j = 0; j < C::KI; ++j) {
+        const int row = (wave * C::KI + j) * C::KRPI + lane / C::KC;
+        const int chunk = (lane % C::KC) ^ k_swz<D>(row);
+        koff[j] = row * (int)ldk * 2 + chunk * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < C::VI; ++j) {
+        const int row = (wave * C::VI + j) * C::VRPI + lane / C::VC;
+        const int chunk = (lane % C::VC) ^ v_swz<DV>(row);
+        voff[j] = row * (int)ldv * 2 + chunk * 16;
+    }
+    auto issue_tile = [&](int T) {
+        const int kb = T * C::TK;
+        const unsigned st = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (T & 1) * C::STAGE);
+        const i32x4 r1 = rsrc(k1, ldk, kb);
+        const i32x4 r2 = rsrc(k2, ldk, kb);
+        const i32x4 rv = rsrc(v, ldv, kb);
+#pragma unroll
+        for (int j = 0; j < C::KI; ++j) {
+            const unsigned dst = st + (wave * C::KI + j) * 1024;
+            copy16_to_lds(r1, dst + C::K1_OFF, koff[j]);
+            copy16_to_lds(r2, dst + C::K2_OFF, koff[j]);
         }
 #pragma unroll
-        for (int i = 0; i < C::VPT; ++i) {
-            const int ch = tid + i * C::THREADS;
-            if (ch < C::VCHUNKS)
-                *reinterpret_cast<uint4*>(base + C::KBYTES + (ch / (DV / 8)) * C::VROW + (ch % (DV / 8)) * 16) = vreg[i];
-        }
+        for (int j = 0; j < C::VI; ++j)
+            copy16_to_lds(rv, st + C::V_OFF + (wave * C::VI + j) * 1024, voff[j]);
     };
 
-    if (ntiles > 0) fetch(0);
-    for (int t = 0; t < ntiles; ++t) {
-        const int stage = t & 1;
-        stash(stage);
-        if (t + 1 < ntiles) fetch(t + 1);
-        __syncthreads();
-
-        const int kb = t * BN;
-        // Skip tiles wholly above this wave's rows (or an idle wave).
-        if (wrow_last < wrow0 || (causal && kb > wrow_last)) continue;
-
-        const unsigned char* kt = smem + stage * C::STAGE;
-        const unsigned char* vt = kt + C::KBYTES;
-        const bool need_mask = (kb + BN > N) || (causal && kb + BN - 1 > wrow0);
-
+    // One key tile: scores, online softmax and both P.V products.
+    auto tile_body = [&](const unsigned char* stg, int sub, int kb, bool masked) {
+        const unsigned char* kt = stg + sub * BN * C::KROWB;
+        const unsigned char* vt = stg + sub * BN * C::VROWB;
         // ---- per map: S^T = K . Q^T, online softmax, P^T fragments --------
         bf16x8 pf[2][2];
 #pragma unroll
@@ -247,17 +296,23 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
             f32x16 s;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = 0.f;
+            // Matrix sections run at raised wave priority: when both waves of
+            // a SIMD are ready, the one feeding the matrix core issues first
+            // and the other wave's softmax fills the gaps.
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int st = 0; st < C::KSTEPS; ++st) {
-                bf16x8 kf = __builtin_bit_cast(bf16x8, load16(kt + k_lane_off + (m * D + st * 16) * 2));
+                bf16x8 kf = __builtin_bit_cast(bf16x8, load16(kt + k_frag[st] + (m ? C::K2_OFF : C::K1_OFF)));
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[m][st], s, 0, 0, 0);
             }
-            if (need_mask) {
+            __builtin_amdgcn_s_setprio(0);
+            // Rare (diagonal / last tile), uniform: kept as a real branch.
+            if (__builtin_expect(masked, 0)) {
+                // key kb + kappa(rho) is visible iff kappa(rho) < lim.
+                const int lim = causal ? min(N - kb, my_row - kb + 1) : N - kb;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb + kappa((r >> 2) * 8 + half * 4 + (r & 3));
-                    if (key >= N || (causal && key > my_row)) s[r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (kappa((r >> 2) * 8 + half * 4 + (r & 3)) >= lim) s[r] = -INFINITY;
             }
             float mx = max3(s[0], s[1], s[2]);
 #pragma unroll
@@ -297,17 +352,38 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
         }
 
         // ---- O^T += V^T . P^T for both maps (shared V fragments) ---------
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int nb = 0; nb < C::VBLK; ++nb) {
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
-                const unsigned char* vp = vt + v_lane_off + t2 * 16 * C::VROW + nb * 64;
+                const unsigned char* vp = vt + v_frag[nb] + t2 * 16 * C::VROWB;
                 bf16x4 lo = lds_read_tr(vp);
-                bf16x4 hi = lds_read_tr(vp + 4 * C::VROW);
+                bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
                 bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][t2], acc[0][nb], 0, 0, 0);
                 acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[1][t2], acc[1][nb], 0, 0, 0);
             }
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    const int ntiles = (kv_end + C::TK - 1) / C::TK;
+    if (ntiles > 0) issue_tile(0);
+    for (int T = 0; T < ntiles; ++T) {
+        // Tile T's copies (the only vector-memory operations in flight) have
+        // landed for this wave; the barrier makes every wave's copies visible
+        // and shows that every wave is done reading the stage copied into next.
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (T + 1 < ntiles) issue_tile(T + 1);
+        const unsigned char* stg = smem + (T & 1) * C::STAGE;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int kb = T * C::TK + sub * BN;
+            // Skip sub-tiles past the keys this wave can see (uniform).
+            if (wrow_last < wrow0 || kb >= kv_end || (causal && kb > wrow_last)) continue;
+            // Only tiles that straddle the diagonal or the sequence end need a mask.
+            tile_body(stg, sub, kb, (kb + BN > N) || (causal && kb + BN - 1 > wrow0));
         }
     }
 
@@ -355,6 +431,13 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)BH * row_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const size_t lds = 2 * (size_t)C::STAGE;
+    static bool attr_set = false;    // raise the dynamic-LDS limit once per process
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, DV, WAVES, OCC>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
     hipLaunchKernelGGL((prefill_bf16_kernel<D, DV, WAVES, OCC>), dim3((unsigned)blocks),
                        dim3(C::THREADS), lds, stream, (const __bf16*)a.q1, (const __bf16*)a.q2,
                        (const __bf16*)a.k1, (const __bf16*)a.k2, (const __bf16*)a.v, a.ldq, a.ldk,

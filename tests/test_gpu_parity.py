@@ -178,6 +178,24 @@ def test_prefill_identical_maps_cancel():
     assert out.abs().max().item() <= 1e-6
 
 
+@pytest.mark.parametrize("B,H,N,causal", [(2, 4, 1000, True), (1, 3, 777, False)])
+def test_prefill_bitwise_deterministic(B, H, N, causal):
+    # Many workgroups, repeated launches: results must be bit-identical, and
+    # with identical maps and lambda = 1 every output must vanish.
+    say("bf16 determinism B=%d H=%d N=%d causal=%s" % (B, H, N, causal))
+    d, dv = 64, 128
+    qh, kh, v = _rand_bf16((B, H, N, d), 31), _rand_bf16((B, H, N, d), 32), _rand_bf16((B, H, N, dv), 33)
+    q, k = _rand_bf16((B, H, N, 2 * d), 34), _rand_bf16((B, H, N, 2 * d), 35)
+    lam = torch.linspace(-0.5, 1.5, H, device=DEV)
+    first = api.diffattn_prefill_packed(q, k, v, lam, causal=causal)
+    for _ in range(3):
+        assert torch.equal(first, api.diffattn_prefill_packed(q, k, v, lam, causal=causal))
+    ones = torch.ones(H, device=DEV)
+    for _ in range(3):
+        z = api.diffattn_prefill(qh, qh, kh, kh, v, ones, causal=causal)
+        assert z.abs().max().item() <= 1e-6
+
+
 def test_prefill_causality_and_determinism():
     B, H, N, d, dv = 1, 2, 400, 64, 128
     say("bf16 causality / determinism")
