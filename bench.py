@@ -48,6 +48,26 @@ def decode_flops(case, lens) -> float:
     return float(sum(int(x) for x in lens)) * (case.Hq // 2) * 6 * case.D
 
 
+PROFILE = os.path.join(ROOT, "profiles", "bench_multineedle64k_v2decode_trace_and_bytes.md")
+
+
+def profiled_traffic(kernel: str):
+    """HBM bytes per launch recorded by the rocprofv3 byte-counter runs in
+    profiles/, or None if the kernel source changed since they were taken."""
+    import hashlib
+    src = {"prefill": "prefill_bf16.hip", "decode": "decode.hip"}[kernel]
+    path = os.path.join(ROOT, "differential_attention_prefill_amd", "csrc", src)
+    try:
+        sha = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+        fields = dict(line.split(": ", 1) for line in open(PROFILE).read().splitlines()
+                      if line.startswith(kernel + "_"))
+    except (OSError, ValueError):
+        return None
+    if fields.get(kernel + "_source_sha256_16", "").strip() != sha:
+        return None
+    return float(fields[kernel + "_traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,7 +190,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic("prefill"),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
             "algorithmic_flops_per_launch": fp,
             "avg_launch_ms": round(pre_ms, 4),
         },
@@ -181,6 +202,7 @@ def main():
             "unit": "GB/s",
             "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
             "algorithmic_bytes_per_launch": bd,
+            "traffic": profiled_traffic("decode"),
             "avg_launch_ms": round(dec_ms, 4),
         },
         "lambda_avg_ms": round(float(np.mean(t_lam)), 4),
