@@ -55,10 +55,12 @@ def profiled_traffic(kernel: str):
     """HBM bytes per launch recorded by the rocprofv3 byte-counter runs in
     profiles/, or None if the kernel source changed since they were taken."""
     import hashlib
-    src = {"prefill": "prefill_bf16.hip", "decode": "decode.hip"}[kernel]
-    path = os.path.join(ROOT, "differential_attention_prefill_amd", "csrc", src)
+    srcs = {"prefill": ("prefill_pp.hip", "bf16_tile.h"), "decode": ("decode.hip",)}[kernel]
     try:
-        sha = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+        h = hashlib.sha256()
+        for src in srcs:
+            h.update(open(os.path.join(ROOT, "differential_attention_prefill_amd", "csrc", src), "rb").read())
+        sha = h.hexdigest()[:16]
         fields = dict(line.split(": ", 1) for line in open(PROFILE).read().splitlines()
                       if line.startswith(kernel + "_"))
     except (OSError, ValueError):
@@ -185,7 +187,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "prefill_bf16_kernel<64,128,4>",
+            "kernel": "prefill_pp_kernel<64,128>",
             "achieved": round(pre_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

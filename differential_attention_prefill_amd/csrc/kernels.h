@@ -42,6 +42,9 @@ hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, c
 
 bool prefill_bf16_supported(int d, int dv);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+// Ping-pong schedule (d <= 64); launch_prefill_bf16 dispatches to it.
+bool prefill_pp_supported(int d, int dv);
+hipError_t launch_prefill_pp(const PrefillArgs& a, hipStream_t stream);
 
 bool prefill_f32_supported(int d, int dv);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);

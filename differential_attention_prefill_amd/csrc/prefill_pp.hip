@@ -1,0 +1,462 @@
+// Fused differential-attention prefill, ping-pong schedule (bf16 in, fp32
+// accumulate; d <= 64).
+//
+// Per head (b,h) and query row i:
+//     A1 = softmax(q1_i K1^T / sqrt d),   A2 = softmax(q2_i K2^T / sqrt d),
+//     o_i = (A1 - lambda_h A2) V,   optional y_i = RMSNorm(o_i) * w * s
+// (page "差分注意力" (aiknowledge.cn), part 一 "差分思路" and part 二 Step 2;
+// per-head normalisation after the difference: "V1 到 V2 的 diff"), in one
+// pass over a shared key/value stream (page "【架构革新】...", section 3: the
+// two softmaxes share intermediates inside one fused kernel).
+//
+// Work split and schedule:
+//  - A workgroup owns 256 query rows of one head, as 8 row blocks of 32, one
+//    per wave.  Each wave runs both maps for its rows: two score tiles, two
+//    running maxima and normalisers, two fp32 accumulators (the maps rescale
+//    independently, so an exact single pass needs one per map).
+//  - Each 32-key sub-tile j is two phases per wave: M(j) issues the matrix
+//    products (P.V of sub-tile j-1 for both maps, then the scores of
+//    sub-tile j for both maps), V(j) runs both online softmaxes of sub-tile
+//    j on the vector ALU.  The waves form two groups, and the second runs one
+//    phase behind the first, with a workgroup barrier after every phase:
+//    while one group's matrix products occupy a SIMD's matrix core, the
+//    other group's softmax occupies its vector ALU.  Waves w and w+4 share a
+//    SIMD and take adjacent row blocks 2w and 2w+1, so they have the same
+//    causal extent and stay balanced.
+//  - Keys and values stream through LDS in tiles of 64 keys, three stages
+//    deep, copied by buffer loads that write LDS directly.  Tile t is read
+//    during global phases 4t .. 4t+5; every wave copies the same number of
+//    1 KB blocks of it, one per phase from phase 4t-6 on, into the stage that
+//    tile t-3 left, and the barrier ending phase 4t-1 publishes them.  Copies
+//    complete in issue order, so a wave waits for an older tile with a fixed
+//    count of newer copies still in flight.
+//  - Tile layout, score orientation (S^T = K . Q^T, a lane holds 16 keys of
+//    one query), the key permutation that lets probabilities feed
+//    O^T += V^T . P^T straight from registers, the transpose load of V, and
+//    the lazy rescale are those of the other bf16 prefill kernel.
+//  - Causal: sub-tiles wholly above a row block are skipped (the wave still
+//    takes part in every barrier); only those that straddle the diagonal or
+//    the sequence end are masked.  Heavy query tiles are scheduled first, and
+//    consecutive workgroups take different heads.
+#include "kernels.h"
+#include "bf16_tile.h"
+
+namespace diffattn {
+namespace {
+
+using namespace tile;
+
+constexpr int PP_WAVES = 8;                  // two groups of four
+constexpr int PP_THREADS = WAVE * PP_WAVES;
+constexpr int PP_BM = QROWS * PP_WAVES;      // 256 rows per workgroup
+constexpr int PP_NSTAGE = 3;
+
+template <int D, int DV>
+struct PPCfg {
+    static constexpr int KC = D / 8;                  // 16-byte chunks per key half-row
+    static constexpr int VC = DV / 8;                 // 16-byte chunks per value row
+    static constexpr int KROWB = D * 2;               // bytes per key half-row (K1 or K2)
+    static constexpr int VROWB = DV * 2;              // bytes per value row
+    static constexpr int K2_OFF = TK * KROWB;         // stage layout: K1 | K2 | V
+    static constexpr int V_OFF = 2 * TK * KROWB;
+    static constexpr int STAGE = 2 * TK * KROWB + TK * VROWB;
+    static constexpr int KBLK = TK * KROWB / 1024;    // 1 KB copy blocks per key half
+    static constexpr int NCOPY = STAGE / 1024;        // copy blocks per tile
+    static constexpr int CPW = NCOPY / PP_WAVES;      // per wave
+    static constexpr int KRPI = 1024 / KROWB;         // key rows per copy block
+    static constexpr int VRPI = 1024 / VROWB;         // value rows per copy block
+    static constexpr int KSTEPS = D / 16;             // MFMA k-steps of one score map
+    static constexpr int VBLK = DV / 32;              // 32-channel blocks of O^T
+    static constexpr int LDS = PP_NSTAGE * STAGE;
+    static_assert(NCOPY % PP_WAVES == 0, "every wave must copy the same number of blocks");
+    static_assert(LDS <= 160 * 1024, "stages exceed LDS");
+};
+
+// Workgroup barrier; the scheduler may not move work across it.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wait until at most CNT of this wave's copies are in flight.
+template <int CNT>
+__device__ __forceinline__ void wait_copies() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
+}
+
+template <int D, int DV>
+__global__ void __launch_bounds__(PP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
+                  const __bf16* __restrict__ k1, const __bf16* __restrict__ k2,
+                  const __bf16* __restrict__ v, int64_t ldq, int64_t ldk, int64_t ldv,
+                  int BH, int H, int N, int causal, const float* __restrict__ lambda,
+                  int rmsnorm, float eps, float norm_scale,
+                  const float* __restrict__ norm_weight, float* __restrict__ out,
+                  int row_tiles) {
+    using C = PPCfg<D, DV>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // Wave-uniform values live in scalar registers: every phase decision is a
+    // scalar branch.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;                 // 0 leads, 1 trails by one phase
+    const int rb = 2 * (wave & 3) + grp;       // row block
+    const int col = lane & 31;                 // query column inside the row block
+    const int half = lane >> 5;                // which 8-element half of a 16-element k-step
+
+    // Consecutive workgroups take consecutive heads (so each XCD sees a fixed
+    // subset of heads); within a head the heaviest causal tiles come first.
+    const int bh = blockIdx.x % BH;
+    const int tile = row_tiles - 1 - (int)(blockIdx.x / BH);
+    const int h = bh % H;
+    const int q0 = tile * PP_BM;
+    const int64_t tok0 = (int64_t)bh * N;
+
+    const int wrow0 = q0 + rb * QROWS;                // first row of the row block
+    const int my_row = wrow0 + col;                   // this lane's query row
+    const int wrow_last = min(wrow0 + QROWS, N) - 1;  // < wrow0 if the block is empty
+
+    const int kv_end = causal ? min(N, q0 + PP_BM) : N;
+    const int nsub = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
+    const int ntile = __builtin_amdgcn_readfirstlane((kv_end + TK - 1) / TK);
+    // This row block sees sub-tiles 0 .. jmax-1.
+    const int jmax = __builtin_amdgcn_readfirstlane(
+        wrow_last < wrow0 ? 0 : (causal ? min(nsub, wrow_last / BN + 1) : nsub));
+
+    // Query fragments of both maps (B operand of S^T = K . Q^T): the lane
+    // holds 8 consecutive elements of its row per 16-element k-step.
+    bf16x8 qf[2][C::KSTEPS];
+    {
+        const bool ok = my_row < N;
+        const int64_t off = (tok0 + (ok ? my_row : 0)) * ldq + half * 8;
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+            qf[0][s] = __builtin_bit_cast(bf16x8, ok ? load16(q1 + off + s * 16) : make_uint4(0, 0, 0, 0));
+            qf[1][s] = __builtin_bit_cast(bf16x8, ok ? load16(q2 + off + s * 16) : make_uint4(0, 0, 0, 0));
+        }
+    }
+    // The query loads land before any copy is issued, so the copy waits
+    // below count copies only.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    const float c = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
+    float mref[2] = {-INFINITY, -INFINITY};   // reference maxima (raw score units)
+    // Growth threshold mref + TAU/c: a new maximum above it triggers a rescale
+    // (-inf until a row has seen a visible key).
+    const float tau_raw = TAU / c;
+    float mthr[2] = {-INFINITY, -INFINITY};
+    float lsum[2] = {0.f, 0.f};               // this lane's share of the normalisers
+    f32x16 acc[2][C::VBLK];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][nb][r] = 0.f;
+    f32x16 s[2];        // scores of the current sub-tile
+    bf16x8 pf[2][2];    // probabilities of the previous sub-tile (B operand)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[m][t][e] = (__bf16)0.f;
+    }
+
+    // ---- lane-constant LDS fragment offsets (stage-relative, sub-tile 0;
+    // sub-tile 1 adds 32 rows, which leaves both swizzles unchanged) --------
+    // K fragment of k-step st: row kappa(col), logical chunk 2*st + half; the
+    // swizzle acts on chunk bits only, so its offset is kx ^ (32*st).
+    const int krow = kappa(col);
+    const int kx = krow * C::KROWB + ((half ^ k_swz<D>(krow)) * 16);
+    // V^T fragment through the transpose load: group g = lane/16 covers
+    // channels 16*(g%2) .. +15 of a 32-channel block and keys 8*(g/2) .. +7 of
+    // a 16-key step; lane j of the group points at key 4*r + j/4, channels
+    // 4*(j%4) .. +3, for the two loads r = 0, 1.  The swizzle acts on chunk
+    // bits below the channel-block bits, so block nb sits at vx ^ (64*nb).
+    const int lg = lane >> 4, gl = lane & 15;
+    const int vrow = (lg >> 1) * 8 + (gl >> 2);
+    const int vx = C::V_OFF + vrow * C::VROWB +
+                   (((2 * (lg & 1) + ((gl & 3) >> 1)) ^ v_swz<DV>(vrow)) * 16) + 8 * (gl & 1);
+
+    // ---- global -> LDS copies ----------------------------------------------
+    // Copy block id (0 .. NCOPY-1) of a tile moves 1 KB: ids below KBLK are
+    // K1 rows, then K2 rows, then V rows, in stage order, so block id lands at
+    // stage + 1024*id.  Wave w copies ids w, w+8, ...  Descriptors start at the
+    // tile's first key and end at the sequence end: rows past N read as zeros.
+    int coff[C::CPW];
+#pragma unroll
+    for (int j = 0; j < C::CPW; ++j) {
+        const int id = wave + PP_WAVES * j;
+        if (id < 2 * C::KBLK) {
+            const int row = (id % C::KBLK) * C::KRPI + lane / C::KC;
+            coff[j] = row * (int)ldk * 2 + (((lane % C::KC) ^ k_swz<D>(row)) * 16);
+        } else {
+            const int row = (id - 2 * C::KBLK) * C::VRPI + lane / C::VC;
+            coff[j] = row * (int)ldv * 2 + (((lane % C::VC) ^ v_swz<DV>(row)) * 16);
+        }
+    }
+    // Copy block b of this wave has a fixed source: its region's base for
+    // this head, the byte stride from one tile to the next, and the row pitch.
+    unsigned long long cbase[C::CPW];
+    unsigned cstride[C::CPW];
+    int cpitch[C::CPW];
+#pragma unroll
+    for (int b = 0; b < C::CPW; ++b) {
+        const int id = wave + PP_WAVES * b;
+        const __bf16* src = id < C::KBLK ? k1 : (id < 2 * C::KBLK ? k2 : v);
+        const int64_t ld = id < 2 * C::KBLK ? ldk : ldv;
+        cbase[b] = (unsigned long long)(src + tok0 * ld);
+        cstride[b] = (unsigned)(TK * ld * 2);
+        cpitch[b] = (int)(ld * 2);
+    }
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    auto issue_block = [&](int t, int b) {
+        // Rows past the sequence end read as zeros (their scores are masked).
+        const int rows = min(N - t * TK, TK);
+        const unsigned st = lds0 + (unsigned)((t % PP_NSTAGE) * C::STAGE);
+#pragma unroll
+        for (int bb = 0; bb < C::CPW; ++bb) {
+            if (bb != b) continue;
+            const i32x4 r = make_rsrc((const void*)(cbase[bb] + (unsigned long long)t * cstride[bb]),
+                                      rows * cpitch[bb]);
+            copy16_to_lds(r, st + (wave + PP_WAVES * bb) * 1024, coff[bb]);
+        }
+    };
+    // Global phase p issues block (p+6) % 4 of tile (p+6) / 4: a tile's blocks
+    // go out one per phase over phases 4t-6 .. 4t-7+CPW, so no phase carries
+    // a burst of copies.  (Tiles 0 and 1 are issued whole before the loop.)
+    auto phase_issue = [&](int p) {
+        const int t = (p + 6) >> 2, b = (p + 6) & 3;
+        if (t >= 2 && t < ntile && b < C::CPW) issue_block(t, b);
+    };
+    // The end of phase 4t-1 waits for tile t.  Tile t+1 then has its first two
+    // blocks in flight (issued at phases 4t-2 and 4t-1); copies complete in
+    // issue order.
+    auto phase_wait = [&](int p) {
+        if (((p + 1) & 3) != 0) return;
+        const int t = (p + 1) >> 2;
+        if (t + 1 < ntile) wait_copies<2>();
+        else wait_copies<0>();
+    };
+    static_assert(C::CPW >= 2 && C::CPW <= 4, "copy schedule assumes 2..4 blocks per wave");
+
+    auto stage_of = [&](int j) -> const unsigned char* {
+        return smem + ((j >> 1) % PP_NSTAGE) * C::STAGE;
+    };
+
+    // M(j): P.V of sub-tile j-1 (both maps share each V^T fragment), then the
+    // scores of sub-tile j for both maps.
+    auto m_phase = [&](int j) {
+        if (j >= 1 && j - 1 < jmax) {
+            const unsigned char* vs = stage_of(j - 1) + ((j - 1) & 1) * BN * C::VROWB;
+#pragma unroll
+            for (int nb = 0; nb < C::VBLK; ++nb) {
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const unsigned char* vp = vs + (vx ^ (64 * nb)) + t2 * 16 * C::VROWB;
+                    const bf16x4 lo = lds_read_tr(vp);
+                    const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
+                    const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][t2], acc[0][nb], 0, 0, 0);
+                    acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[1][t2], acc[1][nb], 0, 0, 0);
+                }
+            }
+        }
+        if (j < jmax) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
+            const unsigned char* ks = stage_of(j) + (j & 1) * BN * C::KROWB;
+#pragma unroll
+            for (int st = 0; st < C::KSTEPS; ++st) {
+                const bf16x8 k1f = __builtin_bit_cast(bf16x8, load16(ks + (kx ^ (32 * st))));
+                const bf16x8 k2f = __builtin_bit_cast(bf16x8, load16(ks + C::K2_OFF + (kx ^ (32 * st))));
+                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[0][st], s[0], 0, 0, 0);
+                s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2f, qf[1][st], s[1], 0, 0, 0);
+            }
+        }
+    };
+
+    // V(j): both online softmaxes of sub-tile j -> probabilities for M(j+1).
+    auto v_phase = [&](int j) {
+        if (j >= jmax) return;
+        const int kb = j * BN;
+        // Rare (diagonal / last sub-tile), uniform: a real branch.
+        if (__builtin_expect((kb + BN > N) || (causal && kb + BN - 1 > wrow0), 0)) {
+            // Register r holds key kb + key_of_reg(r) + 8*half, visible iff
+            // that offset is below lim.
+            const int lim = causal ? min(N - kb, my_row - kb + 1) : N - kb;
+            const int limh = lim - 8 * half;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (key_of_reg(r) >= limh) s[m][r] = -INFINITY;
+        }
+        // Row maxima of both maps: both lanes of a row (16 keys each) and the
+        // reference each accumulator was built on.
+        float mnew[2];
+        bool grow[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            float mx = max3(s[m][0], s[m][1], s[m][2]);
+#pragma unroll
+            for (int r = 3; r < 15; r += 2) mx = max3(mx, s[m][r], s[m][r + 1]);
+            mx = max3(mx, s[m][15], s[m][15]);
+            const f32x2 hm = halves(mx);
+            mnew[m] = max3(mref[m], hm[0], hm[1]);
+            grow[m] = mnew[m] > mthr[m];
+        }
+        // Rare: one uniform branch for both maps keeps the common path in one block.
+        if (__any(grow[0] | grow[1])) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (__any(grow[m])) {
+                    // Lanes that do not grow keep their reference (alpha = 1);
+                    // a first visible key gives alpha = exp2(-inf) = 0 on an
+                    // all-zero accumulator.
+                    const float alpha = grow[m] ? __builtin_amdgcn_exp2f((mref[m] - mnew[m]) * c) : 1.f;
+                    mref[m] = grow[m] ? mnew[m] : mref[m];
+                    mthr[m] = mref[m] + tau_raw;
+                    lsum[m] *= alpha;
+#pragma unroll
+                    for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[m][nb][r] *= alpha;
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const float mc = (mref[m] == -INFINITY) ? 0.f : mref[m] * c;
+            float ls = lsum[m];
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(s[m][t2 * 8 + e], c, -mc)),
+                                      __builtin_amdgcn_exp2f(fmaf(s[m][t2 * 8 + e + 1], c, -mc))};
+                    const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
+                    // The normaliser sums the same bf16 probabilities the product uses.
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, ls, false);
+                    pf[m][t2][e] = pb[0];
+                    pf[m][t2][e + 1] = pb[1];
+                }
+            }
+            lsum[m] = ls;
+        }
+    };
+
+    // ---- the schedule ------------------------------------------------------
+    // Global phase p: group 0 runs M(j) at p = 2j and V(j) at 2j+1, group 1
+    // runs M(j) at 2j+1 and V(j) at 2j+2.  Tile t (sub-tiles 2t, 2t+1) is read
+    // in phases 4t .. 4t+5; its blocks are copied in phases 4t-6 .. 4t-3 into
+    // the stage that tile t-3 left after phase 4t-7, and the barrier ending
+    // phase 4t-1 publishes them.
+#pragma unroll
+    for (int b = 0; b < C::CPW; ++b) issue_block(0, b);
+    if (ntile > 1) {
+#pragma unroll
+        for (int b = 0; b < C::CPW; ++b) issue_block(1, b);
+        wait_copies<C::CPW>();
+    } else {
+        wait_copies<0>();
+    }
+    phase_barrier();            // tile 0 visible
+    if (grp) phase_barrier();   // group 1 starts one phase later
+    for (int j = 0; j <= nsub; ++j) {
+        const int p = 2 * j + grp;
+        phase_issue(p);
+        m_phase(j);
+        phase_wait(p);
+        phase_barrier();
+        phase_issue(p + 1);
+        v_phase(j);
+        phase_wait(p + 1);
+        phase_barrier();
+    }
+    if (!grp) phase_barrier();  // matches group 1's extra barrier
+
+    // ---- epilogue: combine the maps with lambda, optional RMS norm ----------
+    if (my_row >= N) return;
+    const f32x2 h1 = halves(lsum[0]);
+    const f32x2 h2 = halves(lsum[1]);
+    const float w1 = 1.f / (h1[0] + h1[1]);
+    const float w2 = lambda[h] / (h2[0] + h2[1]);
+    float ss = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float y = acc[0][nb][r] * w1 - acc[1][nb][r] * w2;
+            acc[0][nb][r] = y;
+            ss = fmaf(y, y, ss);
+        }
+    float scale = 1.f;
+    if (rmsnorm) {
+        const f32x2 hs = halves(ss);
+        scale = norm_scale / sqrtf((hs[0] + hs[1]) / (float)DV + eps);
+    }
+    float* orow = out + (tok0 + my_row) * DV;
+    // Lane (col, half) holds channels nb*32 + g*8 + half*4 .. +3 in registers
+    // 4g .. 4g+3 of block nb.
+    auto store = [&](auto weight) {
+#pragma unroll
+        for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int ch = nb * 32 + g * 8 + half * 4;
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = acc[0][nb][g * 4 + e] * scale * weight(ch + e);
+                *reinterpret_cast<f32x4*>(orow + ch) = y;
+            }
+    };
+    if (rmsnorm && norm_weight) store([&](int ch) { return norm_weight[ch]; });
+    else store([](int) { return 1.f; });
+}
+
+template <int D, int DV>
+hipError_t launch_pp(const PrefillArgs& a, hipStream_t stream) {
+    using C = PPCfg<D, DV>;
+    const int row_tiles = (a.N + PP_BM - 1) / PP_BM;
+    const int BH = a.B * a.H;
+    const int64_t blocks = (int64_t)BH * row_tiles;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    static bool attr_set = false;    // raise the dynamic-LDS limit once per process
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_pp_kernel<D, DV>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((prefill_pp_kernel<D, DV>), dim3((unsigned)blocks), dim3(PP_THREADS),
+                       (size_t)C::LDS, stream, (const __bf16*)a.q1, (const __bf16*)a.q2,
+                       (const __bf16*)a.k1, (const __bf16*)a.k2, (const __bf16*)a.v, a.ldq, a.ldk,
+                       a.ldv, BH, a.H, a.N, a.causal, a.lambda, a.rmsnorm, a.eps, a.norm_scale,
+                       a.norm_weight, a.out, row_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_pp_supported(int d, int dv) {
+    return (d == 64 && dv == 128) || (d == 64 && dv == 64) || (d == 32 && dv == 64);
+}
+
+hipError_t launch_prefill_pp(const PrefillArgs& a, hipStream_t stream) {
+    if (a.d == 64 && a.dv == 128) return launch_pp<64, 128>(a, stream);
+    if (a.d == 64 && a.dv == 64) return launch_pp<64, 64>(a, stream);
+    if (a.d == 32 && a.dv == 64) return launch_pp<32, 64>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace diffattn
