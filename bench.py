@@ -78,6 +78,8 @@ def main():
     ap.add_argument("--prefill", default="multineedle_64k",
                     choices=["multineedle_64k", "needle_32k", "v1_norm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the layouts measured beside the step (V2 prefill, ...)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -220,10 +222,123 @@ def main():
         result["copy_probe_bytes"] = n
         del src, dst
 
+    if not args.no_extras:
+        del pin, din, q1, q2, k1, k2, v, pout, dout, ws
+        torch.cuda.empty_cache()
+        result["extras"] = measure_extras(dev, max(3, args.steps))
+        pin = din = None
+
     if not args.no_cpu_baseline:
+        if pin is None:
+            pin = W.make_prefill(pcase, device=dev)
+            din = W.make_decode(dcase, device=dev)
         result["cpu_baseline"] = cpu_baseline(pcase, pin, dcase, din, plam, dlam, norm_scale,
                                               args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _time_launches(fn, reps):
+    """Average duration of fn() in ms over `reps` launches, HIP events on the
+    current stream, after one untimed launch."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_extras(dev, reps):
+    """Layouts measured beside the step, each on its own synthetic workload."""
+    import torch
+
+    from differential_attention_prefill_amd import api
+    from differential_attention_prefill_amd import workloads as W
+
+    extras = {}
+    # V2 prefill: doubled query heads over shared K/V heads, D = 128 for both maps.
+    c = W.V2_PREFILL_32K
+    print("# extras: %s" % c.name, file=sys.stderr, flush=True)
+    inp = W.make_prefill_v2(c, device=dev)
+    lam = api.diffattn_lambda(*(inp[k].contiguous() for k in ("lq1", "lk1", "lq2", "lk2")),
+                              layer=c.layer)
+    out = torch.empty((c.B, c.Hq // 2, c.N, c.D), dtype=torch.float32, device=dev)
+    ms = _time_launches(lambda: api.diffattn_prefill_v2(inp["q"], inp["k"], inp["v"], lam,
+                                                        causal=c.causal, out=out), reps)
+    f = float(c.pairs()) * (4 * c.D + 2 * c.D)
+    extras["v2_prefill"] = {"workload": c.name, "avg_launch_ms": round(ms, 4),
+                            "algorithmic_flops_per_launch": f,
+                            "achieved_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+                            "frac_of_bf16_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del inp, out
+    torch.cuda.empty_cache()
+
+    # Unfused two-pass path on the step's prefill workload: single-map
+    # attention for each map (V read twice, two fp32 intermediates), then the
+    # combine pass; beside the fused kernel on the same inputs.
+    c = W.MULTI_NEEDLE_64K
+    print("# extras: unfused vs fused, %s" % c.name, file=sys.stderr, flush=True)
+    inp = W.make_prefill(c, device=dev)
+    d = c.d
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    lam = api.diffattn_lambda(*(inp[x].contiguous() for x in ("lq1", "lk1", "lq2", "lk2")),
+                              layer=c.layer)
+    scale = 1.0 - api.diffattn_lambda_init(c.layer)
+    shape = (c.B, c.H, c.N, c.dv)
+    o1 = torch.empty(shape, dtype=torch.float32, device=dev)
+    o2 = torch.empty(shape, dtype=torch.float32, device=dev)
+    out = torch.empty(shape, dtype=torch.float32, device=dev)
+    fused_ms = _time_launches(lambda: api.diffattn_prefill(
+        q[..., :d], q[..., d:], k[..., :d], k[..., d:], v, lam, causal=True, rmsnorm=c.rmsnorm,
+        eps=c.eps, norm_scale=scale, out=out), reps)
+    att_ms = _time_launches(lambda: (api.diffattn_attention(q[..., :d], k[..., :d], v, out=o1),
+                                     api.diffattn_attention(q[..., d:], k[..., d:], v, out=o2)),
+                            reps)
+    cmb_ms = _time_launches(lambda: api.diffattn_combine(o1, o2, lam, rmsnorm=c.rmsnorm, eps=c.eps,
+                                                         norm_scale=scale, out=out), reps)
+    rows = c.B * c.H * c.N
+    in_bytes = rows * (2 * (2 * d) * 2 + c.dv * 2)          # q and k (both halves), v
+    out_bytes = rows * c.dv * 4
+    inter = 2 * rows * c.dv * 4                              # o1 and o2
+    extras["unfused_vs_fused"] = {
+        "workload": c.name, "fused_ms": round(fused_ms, 4),
+        "unfused_ms": round(att_ms + cmb_ms, 4), "unfused_attention_ms": round(att_ms, 4),
+        "unfused_combine_ms": round(cmb_ms, 4),
+        "fused_speedup": round((att_ms + cmb_ms) / fused_ms, 3),
+        "fused_hbm_bytes_model": in_bytes + out_bytes,
+        "unfused_hbm_bytes_model": in_bytes + rows * c.dv * 2 + 2 * inter + out_bytes,
+        "unfused_extra_device_bytes": inter,
+    }
+    del inp, q, k, v, o1, o2, out
+    torch.cuda.empty_cache()
+
+    # V1-layout decode: half-width maps over per-head K1|K2 and V caches, RMS norm.
+    c = W.V1_DECODE
+    print("# extras: %s" % c.name, file=sys.stderr, flush=True)
+    inp = W.make_decode_v1(c, device=dev)
+    lam = api.diffattn_lambda(*(inp[x].contiguous() for x in ("lq1", "lk1", "lq2", "lk2")),
+                              layer=c.layer)
+    ws = torch.empty(api.diffattn_decode_v1_workspace_bytes(c.B, c.H, c.Lmax), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((c.B, c.H, c.dv), dtype=torch.float32, device=dev)
+    scale = 1.0 - api.diffattn_lambda_init(c.layer)
+    ms = _time_launches(lambda: api.diffattn_decode_v1(
+        inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam, rmsnorm=True, eps=c.eps,
+        norm_scale=scale, workspace=ws, out=out), reps)
+    lens = inp["seq_lens"].cpu().tolist()
+    nbytes = float(sum(int(x) for x in lens)) * c.H * (2 * c.d + c.dv) * 2 + \
+        c.B * c.H * (2 * c.d * 2 + c.dv * 4) + c.H * 4 + c.B * 4
+    extras["v1_decode"] = {"workload": c.name, "avg_launch_ms": round(ms, 4),
+                           "algorithmic_bytes_per_launch": nbytes,
+                           "achieved_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                           "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    del inp, ws, out
+    torch.cuda.empty_cache()
+    return extras
 
 
 def cpu_baseline(pcase, pin, dcase, din, plam, dlam, norm_scale, target_s):

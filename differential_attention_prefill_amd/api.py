@@ -22,8 +22,10 @@ DIFFATTN_BF16 = 1
 STATUS = {0: "DIFFATTN_OK", 1: "DIFFATTN_ERR_INVALID_ARGUMENT", 2: "DIFFATTN_ERR_UNSUPPORTED",
           3: "DIFFATTN_ERR_WORKSPACE", 4: "DIFFATTN_ERR_HIP"}
 
-EXPORTS = ("diffattn_lambda_init", "diffattn_lambda", "diffattn_prefill",
-           "diffattn_decode_workspace_bytes", "diffattn_decode", "diffattn_status_string",
+EXPORTS = ("diffattn_lambda_init", "diffattn_lambda", "diffattn_prefill", "diffattn_prefill_v2",
+           "diffattn_attention", "diffattn_combine",
+           "diffattn_decode_workspace_bytes", "diffattn_decode", "diffattn_decode_v1_workspace_bytes",
+           "diffattn_decode_v1", "diffattn_status_string",
            "diffattn_last_error")
 
 
@@ -52,10 +54,20 @@ def load_library():
     lib.diffattn_prefill.restype = I
     lib.diffattn_prefill.argtypes = [P, P, P, P, P, L, L, L, I, I, I, I, I, I, I, P, I, F, F, P,
                                      P, P]
+    lib.diffattn_prefill_v2.restype = I
+    lib.diffattn_prefill_v2.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P]
+    lib.diffattn_attention.restype = I
+    lib.diffattn_attention.argtypes = [P, P, P, L, L, L, I, I, I, I, I, I, I, P, P]
+    lib.diffattn_combine.restype = I
+    lib.diffattn_combine.argtypes = [P, P, P, I, I, I, I, I, F, F, P, P, P]
     lib.diffattn_decode_workspace_bytes.restype = S
     lib.diffattn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.diffattn_decode.restype = I
     lib.diffattn_decode.argtypes = [P, P, P, P, I, I, I, I, I, P, P, S, P, P]
+    lib.diffattn_decode_v1_workspace_bytes.restype = S
+    lib.diffattn_decode_v1_workspace_bytes.argtypes = [I, I, I]
+    lib.diffattn_decode_v1.restype = I
+    lib.diffattn_decode_v1.argtypes = [P, P, P, P, I, I, I, I, I, P, I, F, F, P, P, S, P, P]
     lib.diffattn_status_string.restype = ctypes.c_char_p
     lib.diffattn_status_string.argtypes = [I]
     lib.diffattn_last_error.restype = ctypes.c_char_p
@@ -162,6 +174,70 @@ def diffattn_prefill_packed(q, k, v, lam, **kw) -> torch.Tensor:
     return diffattn_prefill(q[..., :d], q[..., d:], k[..., :d], k[..., d:], v, lam, **kw)
 
 
+def diffattn_prefill_v2(q, k, v, lam, *, causal: bool = True, out=None, stream=None) -> torch.Tensor:
+    """V2-layout prefill; returns fp32 [B, Hq/2, N, D].
+
+    q: [B, Hq, N, D]; k, v: [B, Hkv, N, D] (bf16 or fp32, contiguous);
+    lam: fp32 [Hq/2].  Pair p uses query heads 2p and 2p+1 over K/V head
+    p // (Hq // (2*Hkv)).
+    """
+    lib = load_library()
+    if q.dtype == torch.bfloat16:
+        dtype = DIFFATTN_BF16
+    elif q.dtype == torch.float32:
+        dtype = DIFFATTN_FP32
+    else:
+        raise ValueError("q must be bf16 or fp32")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != q.dtype or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("%s must be a contiguous 4-d tensor of q's dtype" % name)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, D) or v.shape != (B, Hkv, N, D):
+        raise ValueError("k and v must be [B, Hkv, N, D]")
+    if lam.dtype != torch.float32 or lam.numel() != Hq // 2:
+        raise ValueError("lambda must be fp32 [Hq/2]")
+    if out is None:
+        out = torch.empty((B, Hq // 2, N, D), dtype=torch.float32, device=q.device)
+    _check(lib.diffattn_prefill_v2(_ptr(q), _ptr(k), _ptr(v), dtype, B, Hq, Hkv, N, D,
+                                   1 if causal else 0, _ptr(lam), _ptr(out), _stream(stream)))
+    return out
+
+
+def diffattn_attention(q, k, v, *, causal: bool = True, out=None, stream=None) -> torch.Tensor:
+    """Plain softmax attention softmax(q k^T / sqrt d) v; q, k: [B, H, N, d]
+    and v: [B, H, N, dv] bf16 views with unit channel stride; returns fp32
+    [B, H, N, dv]."""
+    lib = load_library()
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("%s must be bf16" % name)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    ldq, ldk, ldv = _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=torch.float32, device=q.device)
+    _check(lib.diffattn_attention(_ptr(q), _ptr(k), _ptr(v), ldq, ldk, ldv, DIFFATTN_BF16, B, H, N,
+                                  d, dv, 1 if causal else 0, _ptr(out), _stream(stream)))
+    return out
+
+
+def diffattn_combine(o1, o2, lam, *, rmsnorm: bool = False, eps: float = 1e-5,
+                     norm_scale: float = 1.0, norm_weight=None, out=None,
+                     stream=None) -> torch.Tensor:
+    """out = o1 - lambda_h o2 (+ optional RMS norm) on contiguous fp32 [B, H, N, dv]."""
+    lib = load_library()
+    for t, name in ((o1, "o1"), (o2, "o2")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != o1.shape:
+            raise ValueError("%s must be contiguous fp32 of one shape" % name)
+    B, H, N, dv = o1.shape
+    if out is None:
+        out = torch.empty_like(o1)
+    _check(lib.diffattn_combine(_ptr(o1), _ptr(o2), _ptr(lam), B, H, N, dv, 1 if rmsnorm else 0,
+                                eps, norm_scale, _ptr(norm_weight), _ptr(out), _stream(stream)))
+    return out
+
+
 def diffattn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_len: int) -> int:
     return int(load_library().diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len))
 
@@ -191,4 +267,41 @@ def diffattn_decode(q, k_cache, v_cache, seq_lens, lam, *, workspace=None, out=N
                                D, max_len, _ptr(lam), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _ptr(out),
                                _stream(stream)))
+    return out
+
+
+def diffattn_decode_v1_workspace_bytes(B: int, H: int, max_len: int) -> int:
+    return int(load_library().diffattn_decode_v1_workspace_bytes(B, H, max_len))
+
+
+def diffattn_decode_v1(q, k_cache, v_cache, seq_lens, lam, *, rmsnorm: bool = True,
+                       eps: float = 1e-5, norm_scale: float = 1.0, norm_weight=None,
+                       workspace=None, out=None, stream=None) -> torch.Tensor:
+    """V1-layout decode; returns fp32 [B, H, dv].
+
+    q: bf16 [B, H, 2d] packed [q1 | q2]; k_cache: bf16 [B, H, max_len, 2d]
+    packed [k1 | k2]; v_cache: bf16 [B, H, max_len, dv]; seq_lens: int32 [B];
+    lam: fp32 [H].  With ``rmsnorm`` the output rows are RMS-normalised and
+    scaled by ``norm_scale`` (1 - lambda_init for the V1 head norm).
+    """
+    lib = load_library()
+    B, H, d2 = q.shape
+    max_len, dv = k_cache.shape[2], v_cache.shape[-1]
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be contiguous bf16" % name)
+    if k_cache.shape != (B, H, max_len, d2) or v_cache.shape[:3] != (B, H, max_len):
+        raise ValueError("cache shapes must be [B, H, max_len, 2d] and [B, H, max_len, dv]")
+    if seq_lens.dtype != torch.int32 or lam.dtype != torch.float32:
+        raise ValueError("seq_lens must be int32 and lambda fp32")
+    need = diffattn_decode_v1_workspace_bytes(B, H, max_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    _check(lib.diffattn_decode_v1(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, H,
+                                  d2 // 2, dv, max_len, _ptr(lam), 1 if rmsnorm else 0, eps,
+                                  norm_scale, _ptr(norm_weight), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _ptr(out),
+                                  _stream(stream)))
     return out

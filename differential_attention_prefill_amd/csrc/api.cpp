@@ -140,9 +140,148 @@ diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k
     a.norm_scale = norm_scale;
     a.norm_weight = rmsnorm ? norm_weight : nullptr;
     a.out = out;
+    const int64_t HN = (int64_t)H * N;
+    a.hs = {HN * ldq, (int64_t)N * ldq, HN * ldk, (int64_t)N * ldk, HN * ldv, (int64_t)N * ldv, 1};
     hipError_t e = dtype == DIFFATTN_BF16 ? diffattn::launch_prefill_bf16(a, (hipStream_t)stream)
                                           : diffattn::launch_prefill_f32(a, (hipStream_t)stream);
     return hip_status(e, "diffattn_prefill launch");
+}
+
+diffattn_status_t diffattn_prefill_v2(const void* q, const void* k, const void* v,
+                                      diffattn_dtype_t dtype, int B, int Hq, int Hkv, int N, int D,
+                                      int causal, const float* lambda, float* out, void* stream) {
+    if (!q || !k || !v || !lambda || !out)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill_v2: null pointer");
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_prefill_v2: B=%d Hq=%d Hkv=%d N=%d D=%d must be >= 1", B, Hq, Hkv, N, D);
+    if (Hq % (2 * Hkv) != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_prefill_v2: Hq=%d must be a multiple of 2*Hkv=%d", Hq, 2 * Hkv);
+    if (dtype != DIFFATTN_FP32 && dtype != DIFFATTN_BF16)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill_v2: unknown dtype %d", (int)dtype);
+    const int esize = dtype == DIFFATTN_BF16 ? 2 : 4;
+    if ((D * esize) % 16)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_prefill_v2: rows of D=%d elements must be multiples of 16 bytes", D);
+    const void* ptrs[5] = {q, k, v, out, lambda};
+    const char* names[5] = {"q", "k", "v", "out", "lambda"};
+    for (int i = 0; i < 4; ++i)
+        if (!aligned16(ptrs[i]))
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill_v2: %s not 16-byte aligned",
+                        names[i]);
+    if ((reinterpret_cast<uintptr_t>(lambda) & 3u) != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill_v2: lambda not 4-byte aligned");
+    const bool supported = dtype == DIFFATTN_BF16 ? diffattn::prefill_bf16_supported(D, D)
+                                                  : diffattn::prefill_f32_supported(D, D);
+    if (!supported)
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_prefill_v2: D=%d not built for %s", D,
+                    dtype == DIFFATTN_BF16 ? "bf16" : "fp32");
+    if ((int64_t)B * Hq * N > (int64_t)1 << 40)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill_v2: B*Hq*N too large");
+    for (int i = 0; i < 5; ++i) {
+        diffattn_status_t s = check_device(ptrs[i], names[i]);
+        if (s != DIFFATTN_OK) return s;
+    }
+    // Pair p: queries of heads 2p (map 1) and 2p+1 (map 2), over K/V head
+    // p / (Hq / (2 Hkv)) for both maps.
+    const int64_t ND = (int64_t)N * D;
+    diffattn::PrefillArgs a;
+    a.q1 = q;
+    a.q2 = static_cast<const char*>(q) + ND * esize;
+    a.k1 = k; a.k2 = k; a.v = v;
+    a.ldq = D; a.ldk = D; a.ldv = D;
+    a.B = B; a.H = Hq / 2; a.N = N; a.d = D; a.dv = D;
+    a.causal = causal ? 1 : 0;
+    a.lambda = lambda;
+    a.rmsnorm = 0;
+    a.eps = 0.f;
+    a.norm_scale = 1.f;
+    a.norm_weight = nullptr;
+    a.out = out;
+    a.hs = {(int64_t)Hq * ND, 2 * ND, (int64_t)Hkv * ND, ND, (int64_t)Hkv * ND, ND, Hq / (2 * Hkv)};
+    hipError_t e = dtype == DIFFATTN_BF16 ? diffattn::launch_prefill_bf16(a, (hipStream_t)stream)
+                                          : diffattn::launch_prefill_f32(a, (hipStream_t)stream);
+    return hip_status(e, "diffattn_prefill_v2 launch");
+}
+
+diffattn_status_t diffattn_attention(const void* q, const void* k, const void* v, int64_t ldq,
+                                     int64_t ldk, int64_t ldv, diffattn_dtype_t dtype, int B,
+                                     int H, int N, int d, int dv, int causal, float* out,
+                                     void* stream) {
+    if (!q || !k || !v || !out)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_attention: null pointer");
+    if (B < 1 || H < 1 || N < 1 || d < 1 || dv < 1)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_attention: B=%d H=%d N=%d d=%d dv=%d must be >= 1", B, H, N, d, dv);
+    if (dtype != DIFFATTN_BF16)
+        return fail(dtype == DIFFATTN_FP32 ? DIFFATTN_ERR_UNSUPPORTED : DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_attention: bf16 only");
+    if (ldq < d || ldk < d || ldv < dv)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_attention: strides below widths");
+    if ((ldq * 2) % 16 || (ldk * 2) % 16 || (ldv * 2) % 16)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_attention: token strides must be multiples of 16 bytes");
+    const void* ptrs[4] = {q, k, v, out};
+    const char* names[4] = {"q", "k", "v", "out"};
+    for (int i = 0; i < 4; ++i)
+        if (!aligned16(ptrs[i]))
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_attention: %s not 16-byte aligned",
+                        names[i]);
+    if (!diffattn::attention_pp_supported(d, dv))
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_attention: (d=%d, dv=%d) not built", d, dv);
+    if ((int64_t)B * H * N > (int64_t)1 << 40)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_attention: B*H*N too large");
+    for (int i = 0; i < 4; ++i) {
+        diffattn_status_t s = check_device(ptrs[i], names[i]);
+        if (s != DIFFATTN_OK) return s;
+    }
+    diffattn::PrefillArgs a;
+    a.q1 = q; a.q2 = q; a.k1 = k; a.k2 = k; a.v = v;
+    a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
+    a.B = B; a.H = H; a.N = N; a.d = d; a.dv = dv;
+    a.causal = causal ? 1 : 0;
+    a.lambda = nullptr;
+    a.rmsnorm = 0; a.eps = 0.f; a.norm_scale = 1.f; a.norm_weight = nullptr;
+    a.out = out;
+    const int64_t HN = (int64_t)H * N;
+    a.hs = {HN * ldq, (int64_t)N * ldq, HN * ldk, (int64_t)N * ldk, HN * ldv, (int64_t)N * ldv, 1};
+    return hip_status(diffattn::launch_attention_pp(a, (hipStream_t)stream),
+                      "diffattn_attention launch");
+}
+
+diffattn_status_t diffattn_combine(const float* o1, const float* o2, const float* lambda, int B,
+                                   int H, int N, int dv, int rmsnorm, float eps, float norm_scale,
+                                   const float* norm_weight, float* out, void* stream) {
+    if (!o1 || !o2 || !lambda || !out)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_combine: null pointer");
+    if (B < 1 || H < 1 || N < 1 || dv < 1)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_combine: B=%d H=%d N=%d dv=%d must be >= 1", B, H, N, dv);
+    if (rmsnorm && !(eps >= 0.f))
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_combine: eps must be >= 0");
+    const void* ptrs[4] = {o1, o2, lambda, out};
+    const char* names[4] = {"o1", "o2", "lambda", "out"};
+    for (int i = 0; i < 4; ++i)
+        if ((reinterpret_cast<uintptr_t>(ptrs[i]) & 3u) != 0)
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_combine: %s not 4-byte aligned",
+                        names[i]);
+    if (dv != 64 && dv != 128)
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_combine: dv=%d not built", dv);
+    if ((int64_t)B * H * N > (int64_t)1 << 40)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_combine: B*H*N too large");
+    for (int i = 0; i < 4; ++i) {
+        diffattn_status_t s = check_device(ptrs[i], names[i]);
+        if (s != DIFFATTN_OK) return s;
+    }
+    if (rmsnorm && norm_weight) {
+        diffattn_status_t s = check_device(norm_weight, "norm_weight");
+        if (s != DIFFATTN_OK) return s;
+    }
+    return hip_status(diffattn::launch_combine(o1, o2, lambda, B, H, N, dv, rmsnorm ? 1 : 0, eps,
+                                               norm_scale, rmsnorm ? norm_weight : nullptr, out,
+                                               (hipStream_t)stream),
+                      "diffattn_combine launch");
 }
 
 size_t diffattn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len) {
@@ -203,6 +342,75 @@ diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void
     a.workspace = static_cast<float*>(workspace);
     a.out = out;
     return hip_status(diffattn::launch_decode(a, (hipStream_t)stream), "diffattn_decode launch");
+}
+
+size_t diffattn_decode_v1_workspace_bytes(int B, int H, int max_len) {
+    if (B < 1 || H < 1 || max_len < 1) return 0;
+    // Two query columns (one per map) per head.
+    return diffattn::decode_workspace_floats(B, 2 * H, 128, max_len) * sizeof(float);
+}
+
+diffattn_status_t diffattn_decode_v1(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* seq_lens, int B, int H, int d, int dv,
+                                     int max_len, const float* lambda, int rmsnorm, float eps,
+                                     float norm_scale, const float* norm_weight, void* workspace,
+                                     size_t workspace_bytes, float* out, void* stream) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !lambda || !out)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode_v1: null pointer");
+    if (B < 1 || H < 1 || d < 1 || dv < 1 || max_len < 1)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_decode_v1: B=%d H=%d d=%d dv=%d max_len=%d must be >= 1", B, H, d, dv,
+                    max_len);
+    if (rmsnorm && !(eps >= 0.f))
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode_v1: eps must be >= 0");
+    const void* ptrs[6] = {q, k_cache, v_cache, seq_lens, lambda, out};
+    const char* names[6] = {"q", "k_cache", "v_cache", "seq_lens", "lambda", "out"};
+    for (int i = 0; i < 3; ++i)
+        if (!aligned16(ptrs[i]))
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode_v1: %s not 16-byte aligned",
+                        names[i]);
+    for (int i = 3; i < 6; ++i)
+        if ((reinterpret_cast<uintptr_t>(ptrs[i]) & 3u) != 0)
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode_v1: %s not 4-byte aligned",
+                        names[i]);
+    if (rmsnorm && norm_weight && (reinterpret_cast<uintptr_t>(norm_weight) & 3u) != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode_v1: norm_weight not 4-byte aligned");
+    if (!(d == 64 && dv == 128))
+        return fail(DIFFATTN_ERR_UNSUPPORTED,
+                    "diffattn_decode_v1: (d=%d, dv=%d) not built (d=64, dv=128 only)", d, dv);
+    if ((int64_t)B * H * max_len > ((int64_t)1 << 40) || max_len > (1 << 30))
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode_v1: cache too large");
+    const size_t need = diffattn_decode_v1_workspace_bytes(B, H, max_len);
+    if (!workspace || workspace_bytes < need)
+        return fail(DIFFATTN_ERR_WORKSPACE, "diffattn_decode_v1: workspace needs %zu bytes, got %zu",
+                    need, workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_decode_v1: workspace not 256-byte aligned");
+    for (int i = 0; i < 6; ++i) {
+        diffattn_status_t s = check_device(ptrs[i], names[i]);
+        if (s != DIFFATTN_OK) return s;
+    }
+    {
+        diffattn_status_t s = check_device(workspace, "workspace");
+        if (s != DIFFATTN_OK) return s;
+    }
+    if (rmsnorm && norm_weight) {
+        diffattn_status_t s = check_device(norm_weight, "norm_weight");
+        if (s != DIFFATTN_OK) return s;
+    }
+    diffattn::DecodeArgs a;
+    a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.seq_lens = seq_lens;
+    a.B = B; a.Hq = 2 * H; a.Hkv = H; a.D = 2 * d; a.max_len = max_len;
+    a.lambda = lambda;
+    a.workspace = static_cast<float*>(workspace);
+    a.out = out;
+    a.qhalf = d;
+    a.rmsnorm = rmsnorm ? 1 : 0;
+    a.eps = eps;
+    a.norm_scale = norm_scale;
+    a.norm_weight = rmsnorm ? norm_weight : nullptr;
+    return hip_status(diffattn::launch_decode(a, (hipStream_t)stream), "diffattn_decode_v1 launch");
 }
 
 const char* diffattn_status_string(diffattn_status_t status) {

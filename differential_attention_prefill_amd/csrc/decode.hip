@@ -20,7 +20,15 @@
 //    written to the workspace.
 //  - merge kernel: grid (pair, sequence).  Merges the splits of both heads of
 //    a pair by log-sum-exp weights in a fixed order (deterministic), then
-//    combines the two maps with lambda.
+//    combines the two maps with lambda and optionally applies the per-head
+//    RMS norm.
+//
+// V1 layout (half-width maps: q = [q1 | q2] and each key row = [k1 | k2],
+// d = D/2; page "差分注意力", part 一 and "V1 到 V2 的 diff") runs on the same
+// kernels: head h is a group of two query columns over its own K/V rows,
+// column 0 holding q1 in the first d channels and zeros in the rest, column 1
+// zeros then q2, so the D-wide dot products are q1.k1 and q2.k2 and V is read
+// once for both maps.  Scores are scaled by 1/sqrt(d).
 #include "kernels.h"
 
 namespace diffattn {
@@ -53,7 +61,8 @@ __device__ __forceinline__ int slot_key(int rho, int t) { return (rho >> 2) * 8 
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens, int Hq,
-                    int Hkv, int max_len, int max_splits, float* __restrict__ ws) {
+                    int Hkv, int max_len, int max_splits, float* __restrict__ ws, int qhalf,
+                    float c) {
     const int split = blockIdx.x;
     const int g = blockIdx.y;
     const int b = blockIdx.z;
@@ -80,15 +89,19 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
     const bool col_ok = col < G;
 
     const int64_t kv0 = ((int64_t)b * Hkv + g) * max_len;   // row of position 0
-    const float c = 1.4426950408889634f / sqrtf((float)DEC_D);
+    // c = log2(e) / sqrt(dot length), from the host.
 
     // Q^T fragments: lane (col, grp) holds q[head col][s*32 + grp*8 .. +8].
+    // V1 (qhalf > 0): both columns read the packed row [q1 | q2] of head g and
+    // keep only their own half.
     bf16x8 qf[4];
     {
-        const __bf16* qr = q + ((int64_t)b * Hq + g * G + (col_ok ? col : 0)) * DEC_D + grp * 8;
+        const __bf16* qr = qhalf > 0 ? q + ((int64_t)b * Hkv + g) * DEC_D + grp * 8
+                                     : q + ((int64_t)b * Hq + g * G + (col_ok ? col : 0)) * DEC_D + grp * 8;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            uint4 v = col_ok ? ld16(qr + s * 32) : make_uint4(0, 0, 0, 0);
+            const bool mine = qhalf > 0 ? ((s * 32 + grp * 8 < qhalf) == (col == 0)) : true;
+            uint4 v = col_ok && mine ? ld16(qr + s * 32) : make_uint4(0, 0, 0, 0);
             qf[s] = __builtin_bit_cast(bf16x8, v);
         }
     }
@@ -253,7 +266,8 @@ constexpr int MERGE_LDS_SPLITS = 1024;   // splits whose weights are cached in L
 __global__ void __launch_bounds__(MERGE_THREADS)
 decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict__ seq_lens, int Hq,
                     int max_len, int max_splits, const float* __restrict__ lambda,
-                    float* __restrict__ out) {
+                    float* __restrict__ out, int rmsnorm, float eps, float norm_scale,
+                    const float* __restrict__ norm_weight) {
     const int p = blockIdx.x;
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
@@ -295,7 +309,18 @@ decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict__ se
     const float r = acc / l;
     if (m == 1) res[ch] = r;
     __syncthreads();
-    if (m == 0) o[ch] = r - lambda[p] * res[ch];
+    const float y = r - lambda[p] * res[ch];     // meaningful for m == 0
+    if (!rmsnorm) {
+        if (m == 0) o[ch] = y;
+        return;
+    }
+    // RMS norm over the DEC_D channels of the row (threads 0..127, two waves).
+    float ss = m == 0 ? y * y : 0.f;
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((tid & 63) == 0) red[0][tid / 64] = ss;
+    __syncthreads();
+    const float scale = norm_scale / sqrtf((red[0][0] + red[0][1]) / (float)DEC_D + eps);
+    if (m == 0) o[ch] = y * scale * (norm_weight ? norm_weight[ch] : 1.f);
 }
 
 }  // namespace
@@ -312,13 +337,15 @@ size_t decode_workspace_floats(int B, int Hq, int D, int max_len) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (a.D != DEC_D || a.Hq / a.Hkv > DEC_GROUP_MAX) return hipErrorInvalidValue;
     const int S = decode_max_splits(a.max_len);
+    const float c = 1.4426950408889634f / sqrtf((float)(a.qhalf > 0 ? a.qhalf : DEC_D));
     hipLaunchKernelGGL(decode_split_kernel, dim3(S, a.Hkv, a.B), dim3(DEC_THREADS), 0, stream,
                        (const __bf16*)a.q, (const __bf16*)a.k_cache, (const __bf16*)a.v_cache,
-                       a.seq_lens, a.Hq, a.Hkv, a.max_len, S, a.workspace);
+                       a.seq_lens, a.Hq, a.Hkv, a.max_len, S, a.workspace, a.qhalf, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq / 2, a.B), dim3(MERGE_THREADS), 0, stream,
-                       a.workspace, a.seq_lens, a.Hq, a.max_len, S, a.lambda, a.out);
+                       a.workspace, a.seq_lens, a.Hq, a.max_len, S, a.lambda, a.out, a.rmsnorm,
+                       a.eps, a.norm_scale, a.norm_weight);
     return hipGetLastError();
 }
 

@@ -8,7 +8,17 @@
 
 namespace diffattn {
 
-// Arguments of one V1-layout prefill launch, already validated by the caller.
+// Where the rows of diff head (b, h) start, in elements: q1 and q2 at
+// b*qb + h*qh, k1 and k2 at b*kb + g*kh, v at b*vb + g*vh, with K/V head
+// g = h / kv_group.  Rows within a head are ldq / ldk / ldv apart.
+struct HeadStrides {
+    int64_t qb, qh;
+    int64_t kb, kh;
+    int64_t vb, vh;
+    int kv_group;
+};
+
+// Arguments of one prefill launch, already validated by the caller.
 struct PrefillArgs {
     const void* q1;
     const void* q2;
@@ -23,6 +33,7 @@ struct PrefillArgs {
     float eps, norm_scale;
     const float* norm_weight;  // [dv] or nullptr
     float* out;              // [B][H][N][dv]
+    HeadStrides hs;
 };
 
 // Arguments of one V2-layout decode launch, already validated by the caller.
@@ -35,6 +46,12 @@ struct DecodeArgs {
     const float* lambda;     // [Hq/2]
     float* workspace;        // partial states, see decode_workspace_floats
     float* out;              // [B][Hq/2][D]
+    // V1 layout when qhalf > 0: q is [B][Hkv][D] packed [q1 | q2] with
+    // qhalf = d = D/2, Hq = 2*Hkv, and the caches hold [k1 | k2] and v rows.
+    int qhalf = 0;
+    int rmsnorm = 0;
+    float eps = 0.f, norm_scale = 1.f;
+    const float* norm_weight = nullptr;   // [D] or null
 };
 
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
@@ -45,6 +62,15 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 // Ping-pong schedule (d <= 64); launch_prefill_bf16 dispatches to it.
 bool prefill_pp_supported(int d, int dv);
 hipError_t launch_prefill_pp(const PrefillArgs& a, hipStream_t stream);
+// Single-map softmax attention on the same schedule (q1, k1, v; out = A V).
+bool attention_pp_supported(int d, int dv);
+hipError_t launch_attention_pp(const PrefillArgs& a, hipStream_t stream);
+
+// out = o1 - lambda_h * o2 per row of [B][H][N][dv], then the optional RMS
+// norm (rmsnorm, eps, norm_scale, norm_weight as for prefill).
+hipError_t launch_combine(const float* o1, const float* o2, const float* lambda, int B, int H,
+                          int N, int dv, int rmsnorm, float eps, float norm_scale,
+                          const float* norm_weight, float* out, hipStream_t stream);
 
 bool prefill_f32_supported(int d, int dv);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);

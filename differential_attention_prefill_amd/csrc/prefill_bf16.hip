@@ -95,7 +95,7 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
                     int BH, int H, int N, int causal, const float* __restrict__ lambda,
                     int rmsnorm, float eps, float norm_scale,
                     const float* __restrict__ norm_weight, float* __restrict__ out,
-                    int row_tiles) {
+                    int row_tiles, HeadStrides hs) {
     using C = Cfg<D, DV>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -115,7 +115,10 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
     const int tile = row_tiles - 1 - (int)(blockIdx.x / BH);
     const int h = bh % H;
     const int q0 = tile * BM;
-    const int64_t tok0 = (int64_t)bh * N;
+    const int64_t tok0 = (int64_t)bh * N;                 // output rows
+    const int64_t qoff = (bh / H) * hs.qb + h * hs.qh;
+    const int64_t koff = (bh / H) * hs.kb + (h / hs.kv_group) * hs.kh;
+    const int64_t voff = (bh / H) * hs.vb + (h / hs.kv_group) * hs.vh;
 
     const int wrow0 = q0 + rb * QROWS;                // first row of the row block
     const int my_row = wrow0 + col;                   // this lane's query row
@@ -126,7 +129,7 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
     bf16x8 qf[C::KSTEPS];
     {
         const bool ok = my_row < N;
-        const __bf16* qr = (map ? q2 : q1) + (tok0 + (ok ? my_row : 0)) * ldq + half * 8;
+        const __bf16* qr = (map ? q2 : q1) + qoff + (int64_t)(ok ? my_row : 0) * ldq + half * 8;
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s)
             qf[s] = __builtin_bit_cast(bf16x8, ok ? load16(qr + s * 16) : make_uint4(0, 0, 0, 0));
@@ -167,7 +170,7 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
     // rows past N read as zeros (their scores are masked anyway).
     auto rsrc = [&](const __bf16* base, int64_t ld, int kb) {
         const int rows = max(0, min(N - kb, TK));
-        return make_rsrc(base + (tok0 + kb) * ld, rows * (int)ld * 2);
+        return make_rsrc(base + (int64_t)kb * ld, rows * (int)ld * 2);
     };
     int coff[C::CPW];   // lane-constant source offsets of this wave's copies
 #pragma unroll
@@ -184,8 +187,8 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
         const int kb = T * TK;
         const unsigned st = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (T & 1) * C::STAGE);
         if (map == 0) {
-            const i32x4 r1 = rsrc(k1, ldk, kb);
-            const i32x4 r2 = rsrc(k2, ldk, kb);
+            const i32x4 r1 = rsrc(k1 + koff, ldk, kb);
+            const i32x4 r2 = rsrc(k2 + koff, ldk, kb);
 #pragma unroll
             for (int j = 0; j < C::KPW; ++j) {
                 const unsigned dst = st + (rb * C::KPW + j) * 1024;
@@ -193,7 +196,7 @@ prefill_bf16_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2
                 copy16_to_lds(r2, dst + C::K2_OFF, coff[j]);
             }
         } else {
-            const i32x4 rv = rsrc(v, ldv, kb);
+            const i32x4 rv = rsrc(v + voff, ldv, kb);
 #pragma unroll
             for (int j = 0; j < C::VPW; ++j)
                 copy16_to_lds(rv, st + C::V_OFF + (rb * C::VPW + j) * 1024, coff[j]);
@@ -373,7 +376,7 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t stream) {
                        stream, (const __bf16*)a.q1, (const __bf16*)a.q2, (const __bf16*)a.k1,
                        (const __bf16*)a.k2, (const __bf16*)a.v, a.ldq, a.ldk, a.ldv, BH, a.H, a.N,
                        a.causal, a.lambda, a.rmsnorm, a.eps, a.norm_scale, a.norm_weight, a.out,
-                       row_tiles);
+                       row_tiles, a.hs);
     return hipGetLastError();
 }
 

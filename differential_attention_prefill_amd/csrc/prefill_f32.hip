@@ -31,7 +31,7 @@ prefill_f32_kernel(const float* __restrict__ q1, const float* __restrict__ q2,
                    const float* __restrict__ v, int64_t ldq, int64_t ldk, int64_t ldv, int H,
                    int N, int causal, const float* __restrict__ lambda, int rmsnorm, float eps,
                    float norm_scale, const float* __restrict__ norm_weight,
-                   float* __restrict__ out, int row_tiles) {
+                   float* __restrict__ out, int row_tiles, HeadStrides hs) {
     constexpr int DQ = D / 4;    // query/key elements per thread
     constexpr int DVQ = DV / 4;  // output channels per thread
     __shared__ float sk1[F32_BN][D];
@@ -46,13 +46,16 @@ prefill_f32_kernel(const float* __restrict__ q1, const float* __restrict__ q2,
     const int h = bh % H;
     const int row = tile * F32_ROWS + r_local;
     const bool row_ok = row < N;
-    const int64_t head_tok0 = (int64_t)bh * N;
+    const int64_t head_tok0 = (int64_t)bh * N;           // output rows
+    const int64_t qoff = (bh / H) * hs.qb + h * hs.qh;
+    const int64_t koff = (bh / H) * hs.kb + (h / hs.kv_group) * hs.kh;
+    const int64_t voff = (bh / H) * hs.vb + (h / hs.kv_group) * hs.vh;
 
     // Thread `sub` owns elements sub, sub+4, sub+8, ... of each vector.
     float qa[DQ], qb[DQ];
     for (int i = 0; i < DQ; ++i) {
-        qa[i] = row_ok ? q1[(head_tok0 + row) * ldq + sub + 4 * i] : 0.f;
-        qb[i] = row_ok ? q2[(head_tok0 + row) * ldq + sub + 4 * i] : 0.f;
+        qa[i] = row_ok ? q1[qoff + (int64_t)row * ldq + sub + 4 * i] : 0.f;
+        qb[i] = row_ok ? q2[qoff + (int64_t)row * ldq + sub + 4 * i] : 0.f;
     }
     // Scores are kept in raw units; exp(x/sqrt d) = exp2(x * log2(e)/sqrt d).
     const float c = 1.4426950408889634f / sqrtf((float)D);
@@ -69,12 +72,12 @@ prefill_f32_kernel(const float* __restrict__ q1, const float* __restrict__ q2,
         for (int e = tid; e < F32_BN * D; e += F32_THREADS) {
             int j = e / D, cc = e % D;
             bool ok = kb + j < N;
-            sk1[j][cc] = ok ? k1[(head_tok0 + kb + j) * ldk + cc] : 0.f;
-            sk2[j][cc] = ok ? k2[(head_tok0 + kb + j) * ldk + cc] : 0.f;
+            sk1[j][cc] = ok ? k1[koff + (int64_t)(kb + j) * ldk + cc] : 0.f;
+            sk2[j][cc] = ok ? k2[koff + (int64_t)(kb + j) * ldk + cc] : 0.f;
         }
         for (int e = tid; e < F32_BN * DV; e += F32_THREADS) {
             int j = e / DV, cc = e % DV;
-            sv[j][cc] = (kb + j < N) ? v[(head_tok0 + kb + j) * ldv + cc] : 0.f;
+            sv[j][cc] = (kb + j < N) ? v[voff + (int64_t)(kb + j) * ldv + cc] : 0.f;
         }
         __syncthreads();
         const int jn = min(F32_BN, kv_end - kb);
@@ -135,7 +138,7 @@ hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
                        stream, (const float*)a.q1, (const float*)a.q2, (const float*)a.k1,
                        (const float*)a.k2, (const float*)a.v, a.ldq, a.ldk, a.ldv, a.H, a.N,
                        a.causal, a.lambda, a.rmsnorm, a.eps, a.norm_scale, a.norm_weight, a.out,
-                       row_tiles);
+                       row_tiles, a.hs);
     return hipGetLastError();
 }
 

@@ -51,15 +51,18 @@ constexpr int PP_THREADS = WAVE * PP_WAVES;
 constexpr int PP_BM = QROWS * PP_WAVES;      // 256 rows per workgroup
 constexpr int PP_NSTAGE = 3;
 
-template <int D, int DV>
+// MAPS = 2: differential attention (both maps share the K/V stream).
+// MAPS = 1: plain single-map attention with the same schedule, the building
+// block of the unfused two-pass comparison path.
+template <int D, int DV, int MAPS>
 struct PPCfg {
     static constexpr int KC = D / 8;                  // 16-byte chunks per key half-row
     static constexpr int VC = DV / 8;                 // 16-byte chunks per value row
     static constexpr int KROWB = D * 2;               // bytes per key half-row (K1 or K2)
     static constexpr int VROWB = DV * 2;              // bytes per value row
     static constexpr int K2_OFF = TK * KROWB;         // stage layout: K1 | K2 | V
-    static constexpr int V_OFF = 2 * TK * KROWB;
-    static constexpr int STAGE = 2 * TK * KROWB + TK * VROWB;
+    static constexpr int V_OFF = MAPS * TK * KROWB;
+    static constexpr int STAGE = MAPS * TK * KROWB + TK * VROWB;
     static constexpr int KBLK = TK * KROWB / 1024;    // 1 KB copy blocks per key half
     static constexpr int NCOPY = STAGE / 1024;        // copy blocks per tile
     static constexpr int CPW = NCOPY / PP_WAVES;      // per wave
@@ -86,7 +89,7 @@ __device__ __forceinline__ void wait_copies() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
 }
 
-template <int D, int DV>
+template <int D, int DV, int MAPS>
 __global__ void __launch_bounds__(PP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                   const __bf16* __restrict__ k1, const __bf16* __restrict__ k2,
@@ -94,8 +97,8 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                   int BH, int H, int N, int causal, const float* __restrict__ lambda,
                   int rmsnorm, float eps, float norm_scale,
                   const float* __restrict__ norm_weight, float* __restrict__ out,
-                  int row_tiles) {
-    using C = PPCfg<D, DV>;
+                  int row_tiles, HeadStrides hs) {
+    using C = PPCfg<D, DV, MAPS>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int tid = threadIdx.x;
@@ -114,7 +117,11 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     const int tile = row_tiles - 1 - (int)(blockIdx.x / BH);
     const int h = bh % H;
     const int q0 = tile * PP_BM;
-    const int64_t tok0 = (int64_t)bh * N;
+    const int64_t tok0 = (int64_t)bh * N;                 // output rows
+    const int b = bh / H;
+    const int64_t qoff = b * hs.qb + h * hs.qh;
+    const int64_t koff = b * hs.kb + (h / hs.kv_group) * hs.kh;
+    const int64_t voff = b * hs.vb + (h / hs.kv_group) * hs.vh;
 
     const int wrow0 = q0 + rb * QROWS;                // first row of the row block
     const int my_row = wrow0 + col;                   // this lane's query row
@@ -129,14 +136,15 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
 
     // Query fragments of both maps (B operand of S^T = K . Q^T): the lane
     // holds 8 consecutive elements of its row per 16-element k-step.
-    bf16x8 qf[2][C::KSTEPS];
+    bf16x8 qf[MAPS][C::KSTEPS];
     {
         const bool ok = my_row < N;
-        const int64_t off = (tok0 + (ok ? my_row : 0)) * ldq + half * 8;
+        const int64_t off = qoff + (int64_t)(ok ? my_row : 0) * ldq + half * 8;
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
             qf[0][s] = __builtin_bit_cast(bf16x8, ok ? load16(q1 + off + s * 16) : make_uint4(0, 0, 0, 0));
-            qf[1][s] = __builtin_bit_cast(bf16x8, ok ? load16(q2 + off + s * 16) : make_uint4(0, 0, 0, 0));
+            if constexpr (MAPS == 2)
+                qf[1][s] = __builtin_bit_cast(bf16x8, ok ? load16(q2 + off + s * 16) : make_uint4(0, 0, 0, 0));
         }
     }
     // The query loads land before any copy is issued, so the copy waits
@@ -144,23 +152,28 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     __builtin_amdgcn_s_waitcnt(0);
 
     const float c = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
-    float mref[2] = {-INFINITY, -INFINITY};   // reference maxima (raw score units)
+    float mref[MAPS];   // reference maxima (raw score units)
     // Growth threshold mref + TAU/c: a new maximum above it triggers a rescale
     // (-inf until a row has seen a visible key).
     const float tau_raw = TAU / c;
-    float mthr[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.f, 0.f};               // this lane's share of the normalisers
-    f32x16 acc[2][C::VBLK];
+    float mthr[MAPS];
+    float lsum[MAPS];   // this lane's share of the normalisers
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MAPS; ++m) {
+        mref[m] = mthr[m] = -INFINITY;
+        lsum[m] = 0.f;
+    }
+    f32x16 acc[MAPS][C::VBLK];
+#pragma unroll
+    for (int m = 0; m < MAPS; ++m)
 #pragma unroll
         for (int nb = 0; nb < C::VBLK; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][nb][r] = 0.f;
-    f32x16 s[2];        // scores of the current sub-tile
-    bf16x8 pf[2][2];    // probabilities of the previous sub-tile (B operand)
+    f32x16 s[MAPS];       // scores of the current sub-tile
+    bf16x8 pf[MAPS][2];   // probabilities of the previous sub-tile (B operand)
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < MAPS; ++m) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
 #pragma unroll
@@ -194,11 +207,11 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
 #pragma unroll
     for (int j = 0; j < C::CPW; ++j) {
         const int id = wave + PP_WAVES * j;
-        if (id < 2 * C::KBLK) {
+        if (id < MAPS * C::KBLK) {
             const int row = (id % C::KBLK) * C::KRPI + lane / C::KC;
             coff[j] = row * (int)ldk * 2 + (((lane % C::KC) ^ k_swz<D>(row)) * 16);
         } else {
-            const int row = (id - 2 * C::KBLK) * C::VRPI + lane / C::VC;
+            const int row = (id - MAPS * C::KBLK) * C::VRPI + lane / C::VC;
             coff[j] = row * (int)ldv * 2 + (((lane % C::VC) ^ v_swz<DV>(row)) * 16);
         }
     }
@@ -210,9 +223,9 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
 #pragma unroll
     for (int b = 0; b < C::CPW; ++b) {
         const int id = wave + PP_WAVES * b;
-        const __bf16* src = id < C::KBLK ? k1 : (id < 2 * C::KBLK ? k2 : v);
-        const int64_t ld = id < 2 * C::KBLK ? ldk : ldv;
-        cbase[b] = (unsigned long long)(src + tok0 * ld);
+        const __bf16* src = id < C::KBLK ? k1 : (id < MAPS * C::KBLK ? k2 : v);
+        const int64_t ld = id < MAPS * C::KBLK ? ldk : ldv;
+        cbase[b] = (unsigned long long)(src + (id < MAPS * C::KBLK ? koff : voff));
         cstride[b] = (unsigned)(TK * ld * 2);
         cpitch[b] = (int)(ld * 2);
     }
@@ -264,23 +277,25 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                     const bf16x4 lo = lds_read_tr(vp);
                     const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
                     const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][t2], acc[0][nb], 0, 0, 0);
-                    acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[1][t2], acc[1][nb], 0, 0, 0);
+#pragma unroll
+                    for (int m = 0; m < MAPS; ++m)
+                        acc[m][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[m][t2], acc[m][nb], 0, 0, 0);
                 }
             }
         }
         if (j < jmax) {
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+            for (int m = 0; m < MAPS; ++m)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
             const unsigned char* ks = stage_of(j) + (j & 1) * BN * C::KROWB;
 #pragma unroll
             for (int st = 0; st < C::KSTEPS; ++st) {
-                const bf16x8 k1f = __builtin_bit_cast(bf16x8, load16(ks + (kx ^ (32 * st))));
-                const bf16x8 k2f = __builtin_bit_cast(bf16x8, load16(ks + C::K2_OFF + (kx ^ (32 * st))));
-                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[0][st], s[0], 0, 0, 0);
-                s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2f, qf[1][st], s[1], 0, 0, 0);
+#pragma unroll
+                for (int m = 0; m < MAPS; ++m) {
+                    const bf16x8 kf = __builtin_bit_cast(bf16x8, load16(ks + m * C::K2_OFF + (kx ^ (32 * st))));
+                    s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[m][st], s[m], 0, 0, 0);
+                }
             }
         }
     };
@@ -296,17 +311,18 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             const int lim = causal ? min(N - kb, my_row - kb + 1) : N - kb;
             const int limh = lim - 8 * half;
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+            for (int m = 0; m < MAPS; ++m)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (key_of_reg(r) >= limh) s[m][r] = -INFINITY;
         }
         // Row maxima of both maps: both lanes of a row (16 keys each) and the
         // reference each accumulator was built on.
-        float mnew[2];
-        bool grow[2];
+        float mnew[MAPS];
+        bool grow[MAPS];
+        bool any_grow = false;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < MAPS; ++m) {
             float mx = max3(s[m][0], s[m][1], s[m][2]);
 #pragma unroll
             for (int r = 3; r < 15; r += 2) mx = max3(mx, s[m][r], s[m][r + 1]);
@@ -314,11 +330,12 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             const f32x2 hm = halves(mx);
             mnew[m] = max3(mref[m], hm[0], hm[1]);
             grow[m] = mnew[m] > mthr[m];
+            any_grow = any_grow | grow[m];
         }
         // Rare: one uniform branch for both maps keeps the common path in one block.
-        if (__any(grow[0] | grow[1])) {
+        if (__any(any_grow)) {
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
+            for (int m = 0; m < MAPS; ++m) {
                 if (__any(grow[m])) {
                     // Lanes that do not grow keep their reference (alpha = 1);
                     // a first visible key gives alpha = exp2(-inf) = 0 on an
@@ -335,7 +352,7 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             }
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < MAPS; ++m) {
             const float mc = (mref[m] == -INFINITY) ? 0.f : mref[m] * c;
             float ls = lsum[m];
 #pragma unroll
@@ -388,20 +405,27 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // ---- epilogue: combine the maps with lambda, optional RMS norm ----------
     if (my_row >= N) return;
     const f32x2 h1 = halves(lsum[0]);
-    const f32x2 h2 = halves(lsum[1]);
     const float w1 = 1.f / (h1[0] + h1[1]);
-    const float w2 = lambda[h] / (h2[0] + h2[1]);
     float ss = 0.f;
+    if constexpr (MAPS == 2) {
+        const f32x2 h2 = halves(lsum[1]);
+        const float w2 = lambda[h] / (h2[0] + h2[1]);
 #pragma unroll
-    for (int nb = 0; nb < C::VBLK; ++nb)
+        for (int nb = 0; nb < C::VBLK; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float y = acc[0][nb][r] * w1 - acc[1][nb][r] * w2;
-            acc[0][nb][r] = y;
-            ss = fmaf(y, y, ss);
-        }
+            for (int r = 0; r < 16; ++r) {
+                const float y = acc[0][nb][r] * w1 - acc[1][nb][r] * w2;
+                acc[0][nb][r] = y;
+                ss = fmaf(y, y, ss);
+            }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[0][nb][r] *= w1;
+    }
     float scale = 1.f;
-    if (rmsnorm) {
+    if (MAPS == 2 && rmsnorm) {
         const f32x2 hs = halves(ss);
         scale = norm_scale / sqrtf((hs[0] + hs[1]) / (float)DV + eps);
     }
@@ -420,29 +444,29 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                 *reinterpret_cast<f32x4*>(orow + ch) = y;
             }
     };
-    if (rmsnorm && norm_weight) store([&](int ch) { return norm_weight[ch]; });
+    if (MAPS == 2 && rmsnorm && norm_weight) store([&](int ch) { return norm_weight[ch]; });
     else store([](int) { return 1.f; });
 }
 
-template <int D, int DV>
+template <int D, int DV, int MAPS>
 hipError_t launch_pp(const PrefillArgs& a, hipStream_t stream) {
-    using C = PPCfg<D, DV>;
+    using C = PPCfg<D, DV, MAPS>;
     const int row_tiles = (a.N + PP_BM - 1) / PP_BM;
     const int BH = a.B * a.H;
     const int64_t blocks = (int64_t)BH * row_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     static bool attr_set = false;    // raise the dynamic-LDS limit once per process
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_pp_kernel<D, DV>,
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_pp_kernel<D, DV, MAPS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((prefill_pp_kernel<D, DV>), dim3((unsigned)blocks), dim3(PP_THREADS),
+    hipLaunchKernelGGL((prefill_pp_kernel<D, DV, MAPS>), dim3((unsigned)blocks), dim3(PP_THREADS),
                        (size_t)C::LDS, stream, (const __bf16*)a.q1, (const __bf16*)a.q2,
                        (const __bf16*)a.k1, (const __bf16*)a.k2, (const __bf16*)a.v, a.ldq, a.ldk,
                        a.ldv, BH, a.H, a.N, a.causal, a.lambda, a.rmsnorm, a.eps, a.norm_scale,
-                       a.norm_weight, a.out, row_tiles);
+                       a.norm_weight, a.out, row_tiles, a.hs);
     return hipGetLastError();
 }
 
@@ -453,9 +477,19 @@ bool prefill_pp_supported(int d, int dv) {
 }
 
 hipError_t launch_prefill_pp(const PrefillArgs& a, hipStream_t stream) {
-    if (a.d == 64 && a.dv == 128) return launch_pp<64, 128>(a, stream);
-    if (a.d == 64 && a.dv == 64) return launch_pp<64, 64>(a, stream);
-    if (a.d == 32 && a.dv == 64) return launch_pp<32, 64>(a, stream);
+    if (a.d == 64 && a.dv == 128) return launch_pp<64, 128, 2>(a, stream);
+    if (a.d == 64 && a.dv == 64) return launch_pp<64, 64, 2>(a, stream);
+    if (a.d == 32 && a.dv == 64) return launch_pp<32, 64, 2>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+bool attention_pp_supported(int d, int dv) {
+    return (d == 64 && dv == 128) || (d == 64 && dv == 64);
+}
+
+hipError_t launch_attention_pp(const PrefillArgs& a, hipStream_t stream) {
+    if (a.d == 64 && a.dv == 128) return launch_pp<64, 128, 1>(a, stream);
+    if (a.d == 64 && a.dv == 64) return launch_pp<64, 64, 1>(a, stream);
     return hipErrorInvalidValue;
 }
 

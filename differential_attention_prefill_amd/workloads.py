@@ -75,6 +75,56 @@ class DecodeCase:
         return torch.float32 if self.dtype == "fp32" else torch.bfloat16
 
 
+@dataclasses.dataclass(frozen=True)
+class V2PrefillCase:
+    """A V2-layout prefill workload: Hq query heads (pairs 2p, 2p+1) over Hkv
+    shared K/V heads, full head width D for both maps, no per-head norm."""
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    D: int
+    layer: int
+    seed: int
+    causal: bool = True
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    @property
+    def pairs_per_kv(self) -> int:
+        return self.Hq // (2 * self.Hkv)
+
+    def pairs(self) -> int:
+        per_head = self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+        return self.B * (self.Hq // 2) * per_head
+
+
+@dataclasses.dataclass(frozen=True)
+class V1DecodeCase:
+    """A V1-layout decode workload: per head one packed query [q1 | q2] over a
+    cache of packed keys [k1 | k2] and values, RMS-normalised output."""
+    name: str
+    B: int
+    H: int
+    d: int
+    dv: int
+    Lmin: int
+    Lmax: int
+    layer: int
+    seed: int
+    rmsnorm: bool = True
+    eps: float = 1e-5
+    dtype: str = "bf16"
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+
 # The five workloads the operator is specified on.
 TINY_FP32 = PrefillCase("tiny_fp32_b1_h2_n128_d32_dv64", "fp32", B=1, H=2, N=128, d=32, dv=64,
                         layer=1, rmsnorm=False, seed=1)
@@ -88,6 +138,16 @@ V2_DECODE = DecodeCase("v2_decode_bf16_b32_hq32_hkv8_d128_l4096_65536", B=32, Hq
 MULTI_NEEDLE_64K = PrefillCase("multineedle_bf16_b1_h32_n65536_d64_dv128", "bf16", B=1, H=32,
                                N=65536, d=64, dv=128, layer=12, rmsnorm=True, seed=5,
                                needle="mean_query", n_needles=20)
+
+# The V2 (production) prefill layout at long context: 16 pairs over 8 K/V
+# heads, head width 128 for both maps.
+V2_PREFILL_32K = V2PrefillCase("v2_prefill_bf16_b1_hq32_hkv8_n32768_d128", "bf16", B=1, Hq=32,
+                               Hkv=8, N=32768, D=128, layer=1, seed=6)
+
+# V1-layout decode: 16 diff heads with their own half-width K1|K2 and V
+# caches (twice the cache bytes of the V2 layout's 8 shared KV heads).
+V1_DECODE = V1DecodeCase("v1_decode_bf16_b16_h16_d64_dv128_l4096_65536", B=16, H=16, d=64, dv=128,
+                         Lmin=4096, Lmax=65536, layer=12, seed=7)
 
 PREFILL_CASES = {c.name: c for c in (TINY_FP32, V1_NORM, NEEDLE_32K, MULTI_NEEDLE_64K)}
 DECODE_CASES = {V2_DECODE.name: V2_DECODE}
@@ -168,6 +228,39 @@ def make_decode(case: DecodeCase, device="cpu", fill_unused: Optional[float] = N
         for b in range(B):
             kc[b, :, int(lens[b]):, :] = fill_unused
             vc[b, :, int(lens[b]):, :] = fill_unused
+    return {"q": q, "k_cache": kc, "v_cache": vc, "seq_lens": lens, "lq1": lam[0],
+            "lk1": lam[1], "lq2": lam[2], "lk2": lam[3]}
+
+
+def make_prefill_v2(case: V2PrefillCase, device="cpu") -> dict:
+    """Inputs of one V2 prefill workload: q [B, Hq, N, D]; k, v [B, Hkv, N, D];
+    lq1, lk1, lq2, lk2 fp32 [Hq/2, D]."""
+    g = _gen(case.seed, device)
+    dt = case.torch_dtype
+    q = _normal((case.B, case.Hq, case.N, case.D), g, device, dt)
+    k = _normal((case.B, case.Hkv, case.N, case.D), g, device, dt)
+    v = _normal((case.B, case.Hkv, case.N, case.D), g, device, dt)
+    lam = [_normal((case.Hq // 2, case.D), g, device, torch.float32, std=0.1) for _ in range(4)]
+    return {"q": q, "k": k, "v": v, "lq1": lam[0], "lk1": lam[1], "lq2": lam[2], "lk2": lam[3]}
+
+
+def make_decode_v1(case: V1DecodeCase, device="cpu") -> dict:
+    """Inputs of one V1 decode workload: q [B, H, 2d]; k_cache [B, H, Lmax, 2d];
+    v_cache [B, H, Lmax, dv]; seq_lens int32 [B] uniform in [Lmin, Lmax];
+    lq1, lk1, lq2, lk2 fp32 [H, d]."""
+    g = _gen(case.seed, device)
+    dt = case.torch_dtype
+    B, H, d, dv, L = case.B, case.H, case.d, case.dv, case.Lmax
+    q = _normal((B, H, 2 * d), g, device, dt)
+    kc = torch.empty((B, H, L, 2 * d), dtype=dt, device=device)
+    vc = torch.empty((B, H, L, dv), dtype=dt, device=device)
+    for b in range(B):
+        kc[b] = _normal((H, L, 2 * d), g, device, dt)
+    for b in range(B):
+        vc[b] = _normal((H, L, dv), g, device, dt)
+    lam = [_normal((H, d), g, device, torch.float32, std=0.1) for _ in range(4)]
+    lens = torch.randint(case.Lmin, case.Lmax + 1, (B,), generator=g, device=device,
+                         dtype=torch.int64).to(torch.int32)
     return {"q": q, "k_cache": kc, "v_cache": vc, "seq_lens": lens, "lq1": lam[0],
             "lk1": lam[1], "lq2": lam[2], "lk2": lam[3]}
 

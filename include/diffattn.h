@@ -103,6 +103,53 @@ diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k
                                    float* out, void* stream);
 
 /*
+ * Fused differential-attention prefill, V2 layout (page "差分注意力",
+ * "V1 到 V2 的 diff": the query heads are doubled over a shared key/value
+ * cache, each map keeps the full head width, and no per-head norm follows).
+ * Diff head (pair) p takes query heads 2p (map 1) and 2p+1 (map 2); both maps
+ * use K/V head g = p / (Hq / (2*Hkv)) (grouped-query sharing).
+ *   q      : device [B][Hq][N][D] (dtype)
+ *   k, v   : device [B][Hkv][N][D] (dtype)
+ *   lambda : device fp32 [Hq/2]
+ *   out    : device fp32 [B][Hq/2][N][D]
+ * out[b,p,n] = (A1 - lambda_p A2) V with A1, A2 the softmaxes of the two
+ * maps' scores / sqrt(D); causal != 0 restricts query n to keys 0..n.
+ * Supported: BF16 and FP32 with D in {64, 128} (UNSUPPORTED otherwise).
+ * Hq must be a multiple of 2*Hkv, pointers 16-byte aligned, D*sizeof(elem)
+ * a multiple of 16 (INVALID_ARGUMENT otherwise).  Asynchronous on stream.
+ */
+diffattn_status_t diffattn_prefill_v2(const void* q, const void* k, const void* v,
+                                      diffattn_dtype_t dtype, int B, int Hq, int Hkv, int N, int D,
+                                      int causal, const float* lambda, float* out, void* stream);
+
+/*
+ * Plain single-map softmax attention, out = softmax(q k^T / sqrt d) v, on the
+ * prefill kernel's schedule.  With diffattn_combine it forms the unfused
+ * two-pass differential attention that the fused kernels replace (page
+ * "【架构革新】...", section 3: separate passes keep two full intermediate
+ * outputs and read the values twice; page "差分注意力", "V1 到 V2 的 diff").
+ * Layouts as for diffattn_prefill: q, k [B][H][N][ld] with d columns, v with
+ * dv columns, out fp32 [B][H][N][dv].  causal != 0: query n sees keys 0..n.
+ * Supported: BF16 with (d, dv) in {(64,128), (64,64)}; FP32 and other
+ * shapes return UNSUPPORTED.  Other errors as for diffattn_prefill.
+ */
+diffattn_status_t diffattn_attention(const void* q, const void* k, const void* v, int64_t ldq,
+                                     int64_t ldk, int64_t ldv, diffattn_dtype_t dtype, int B,
+                                     int H, int N, int d, int dv, int causal, float* out,
+                                     void* stream);
+
+/*
+ * Second pass of the unfused path: out = o1 - lambda_h * o2 row by row over
+ * fp32 [B][H][N][dv] tensors (page "差分注意力", part 一 "差分思路"), then the
+ * optional RMS norm exactly as in diffattn_prefill.  lambda: device fp32 [H].
+ * out may alias o1.  Supported dv: 64, 128 (UNSUPPORTED otherwise); pointers
+ * 4-byte aligned (INVALID_ARGUMENT otherwise).
+ */
+diffattn_status_t diffattn_combine(const float* o1, const float* o2, const float* lambda, int B,
+                                   int H, int N, int dv, int rmsnorm, float eps, float norm_scale,
+                                   const float* norm_weight, float* out, void* stream);
+
+/*
  * Bytes of device workspace diffattn_decode needs for these sizes (partial
  * softmax states of every KV split).  Returns 0 for invalid sizes.
  */
@@ -132,6 +179,39 @@ diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void
                                   const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
                                   int max_len, const float* lambda, void* workspace,
                                   size_t workspace_bytes, float* out, void* stream);
+
+/*
+ * Bytes of device workspace diffattn_decode_v1 needs (two partial softmax
+ * states, one per map, per head and KV split).  Returns 0 for invalid sizes.
+ */
+size_t diffattn_decode_v1_workspace_bytes(int B, int H, int max_len);
+
+/*
+ * Split-KV differential-attention decode, V1 layout (page "差分注意力", part 一
+ * "差分思路" and "V1 到 V2 的 diff": half-width maps and per-head RMS norm).
+ * One query token per sequence and head, attending to cache positions
+ * 0 .. seq_lens[b]-1; the value cache is read once for both maps.
+ *   q        : bf16 [B][H][2d], packed [q1 | q2]
+ *   k_cache  : bf16 [B][H][max_len][2d], packed [k1 | k2]
+ *   v_cache  : bf16 [B][H][max_len][dv]
+ *   seq_lens : device int32 [B], each in [1, max_len]
+ *   lambda   : device fp32 [H]
+ *   out      : device fp32 [B][H][dv]
+ * out = (softmax(q1 K1^T / sqrt d) - lambda_h softmax(q2 K2^T / sqrt d)) V,
+ * then, if rmsnorm != 0, y_c = out_c / sqrt(mean_c out_c^2 + eps) * w_c *
+ * norm_scale with w = norm_weight (device fp32 [dv]) or 1 when NULL; pass
+ * norm_scale = 1 - lambda_init.
+ * Supported: d = 64, dv = 128 (UNSUPPORTED otherwise).  workspace: device
+ * memory of at least diffattn_decode_v1_workspace_bytes(B, H, max_len)
+ * bytes, 256-byte aligned, owned by the caller (WORKSPACE if missing or
+ * small).  A sequence whose device-side length is outside [1, max_len]
+ * yields zeros.  Other argument errors as for diffattn_decode.
+ */
+diffattn_status_t diffattn_decode_v1(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* seq_lens, int B, int H, int d, int dv,
+                                     int max_len, const float* lambda, int rmsnorm, float eps,
+                                     float norm_scale, const float* norm_weight, void* workspace,
+                                     size_t workspace_bytes, float* out, void* stream);
 
 /* Static text for a status code. */
 const char* diffattn_status_string(diffattn_status_t status);

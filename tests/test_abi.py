@@ -85,6 +85,27 @@ def test_prefill_validation(lib, kw, code):
     assert lib.diffattn_last_error().decode()
 
 
+def _prefill_v2(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, B=1, Hq=8, Hkv=2, N=16, D=128, causal=1, lam=FAKE,
+             out=FAKE, stream=None)
+    a.update(kw)
+    return lib.diffattn_prefill_v2(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["Hq"], a["Hkv"],
+                                   a["N"], a["D"], a["causal"], a["lam"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(lam=None), INVALID),
+    (dict(out=None), INVALID), (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(Hkv=0), INVALID),
+    (dict(Hq=6), INVALID), (dict(Hq=8, Hkv=3), INVALID), (dict(dtype=7), INVALID),
+    (dict(D=100), INVALID), (dict(q=FAKE + 2), INVALID), (dict(v=FAKE + 8), INVALID),
+    (dict(lam=FAKE + 2), INVALID),
+    (dict(D=48), UNSUPPORTED), (dict(D=32), UNSUPPORTED), (dict(dtype=0, D=32), UNSUPPORTED),
+])
+def test_prefill_v2_validation(lib, kw, code):
+    assert _prefill_v2(lib, **kw) == code
+    assert lib.diffattn_last_error().decode()
+
+
 def _decode(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, B=2, Hq=8, Hkv=2, D=128, max_len=4096,
              lam=FAKE, ws=FAKE, ws_bytes=1 << 30, out=FAKE, stream=None)
@@ -103,6 +124,66 @@ def _decode(lib, **kw):
 ])
 def test_decode_validation(lib, kw, code):
     assert _decode(lib, **kw) == code
+
+
+def _attention(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ldq=128, ldk=128, ldv=128, dtype=1, B=1, H=2, N=16, d=64,
+             dv=128, causal=1, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.diffattn_attention(a["q"], a["k"], a["v"], a["ldq"], a["ldk"], a["ldv"], a["dtype"],
+                                  a["B"], a["H"], a["N"], a["d"], a["dv"], a["causal"], a["out"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(B=0), INVALID), (dict(dtype=5), INVALID),
+    (dict(ldq=32), INVALID), (dict(ldv=100), INVALID), (dict(k=FAKE + 2), INVALID),
+    (dict(dtype=0), UNSUPPORTED), (dict(d=32, ldq=64, ldk=64, dv=64, ldv=64), UNSUPPORTED),
+    (dict(d=128, ldq=128, ldk=128), UNSUPPORTED),
+])
+def test_attention_validation(lib, kw, code):
+    assert _attention(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o1=None), INVALID), (dict(lam=None), INVALID), (dict(N=0), INVALID),
+    (dict(o2=FAKE + 2), INVALID), (dict(rmsnorm=1, eps=-1.0), INVALID), (dict(dv=96), UNSUPPORTED),
+])
+def test_combine_validation(lib, kw, code):
+    a = dict(o1=FAKE, o2=FAKE, lam=FAKE, B=1, H=2, N=8, dv=128, rmsnorm=0, eps=1e-5, scale=1.0,
+             w=None, out=FAKE)
+    a.update(kw)
+    assert lib.diffattn_combine(a["o1"], a["o2"], a["lam"], a["B"], a["H"], a["N"], a["dv"],
+                                a["rmsnorm"], a["eps"], a["scale"], a["w"], a["out"], None) == code
+
+
+def _decode_v1(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, B=2, H=4, d=64, dv=128, max_len=4096, lam=FAKE,
+             rmsnorm=1, eps=1e-5, scale=0.5, w=None, ws=FAKE, ws_bytes=1 << 30, out=FAKE,
+             stream=None)
+    a.update(kw)
+    return lib.diffattn_decode_v1(a["q"], a["k"], a["v"], a["lens"], a["B"], a["H"], a["d"],
+                                  a["dv"], a["max_len"], a["lam"], a["rmsnorm"], a["eps"],
+                                  a["scale"], a["w"], a["ws"], a["ws_bytes"], a["out"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(lens=None), INVALID), (dict(out=None), INVALID),
+    (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(max_len=0), INVALID),
+    (dict(k=FAKE + 8), INVALID), (dict(lens=FAKE + 2), INVALID), (dict(ws=FAKE + 16), INVALID),
+    (dict(eps=-1.0), INVALID), (dict(w=FAKE + 2), INVALID),
+    (dict(d=32), UNSUPPORTED), (dict(dv=64), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+])
+def test_decode_v1_validation(lib, kw, code):
+    assert _decode_v1(lib, **kw) == code
+
+
+def test_decode_v1_workspace_size(lib):
+    n = api.diffattn_decode_v1_workspace_bytes(16, 16, 65536)
+    assert n == api.diffattn_decode_workspace_bytes(16, 32, 16, 128, 65536)
+    assert api.diffattn_decode_v1_workspace_bytes(16, 0, 65536) == 0
 
 
 def test_decode_workspace_size(lib):

@@ -148,6 +148,107 @@ def test_prefill_long_workloads_sampled(case):
 
 
 # ---------------------------------------------------------------------------
+# V2-layout prefill: doubled query heads over shared K/V heads
+# ---------------------------------------------------------------------------
+
+def _v2_pair_tensors(inp, case):
+    """Per-pair tensors [B, Hq/2, N, D]: q1 = heads 2p, q2 = heads 2p+1, k1 = k2
+    and v the K/V head p // (Hq / (2 Hkv)) (test-side marshalling only)."""
+    q = inp["q"]
+    g = case.pairs_per_kv
+    k = inp["k"].repeat_interleave(g, dim=1)
+    v = inp["v"].repeat_interleave(g, dim=1)
+    return (q[:, 0::2].contiguous(), q[:, 1::2].contiguous(), k.contiguous(), k.contiguous(),
+            v.contiguous())
+
+
+def _v2_check(case, rows=None):
+    inp = W.make_prefill_v2(case, device=DEV)
+    lam_gpu = gpu_lambda(inp, case.layer)
+    out = api.diffattn_prefill_v2(inp["q"], inp["k"], inp["v"], lam_gpu, causal=case.causal)
+    torch.cuda.synchronize()
+    q1, q2, k1, k2, v = (t.cpu() for t in _v2_pair_tensors(inp, case))
+    got = out.cpu().numpy()
+    if rows is not None:
+        got = got.reshape(-1, case.D)[rows]
+    ref = oracle.prefill(q1, q2, k1, k2, v, lam_gpu.cpu().numpy(), causal=case.causal, rows=rows)
+    return compare(got, ref, case.dtype, case.name)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,N,D,causal", [
+    ("bf16", 8, 2, 300, 128, True), ("bf16", 8, 4, 200, 64, True), ("bf16", 4, 1, 129, 128, False),
+    ("bf16", 16, 2, 97, 128, True), ("fp32", 4, 1, 130, 64, True), ("fp32", 8, 2, 65, 128, False),
+])
+def test_prefill_v2_shapes(dtype, Hq, Hkv, N, D, causal):
+    case = W.V2PrefillCase("v2_%s_hq%d_hkv%d_n%d_d%d" % (dtype, Hq, Hkv, N, D), dtype, B=2, Hq=Hq,
+                           Hkv=Hkv, N=N, D=D, layer=2, seed=3000 + N, causal=causal)
+    say("v2 prefill %s causal=%s" % (case.name, causal))
+    _v2_check(case)
+
+
+def test_prefill_v2_long_sampled():
+    case = W.scaled_prefill(W.V2_PREFILL_32K, N=8192)
+    say("v2 prefill %s (sampled rows)" % case.name)
+    g = np.random.default_rng(1)
+    H = case.Hq // 2
+    rows = np.concatenate([h * case.N + np.unique(np.concatenate(
+        [[0, 1, 127, 128, case.N - 1], g.integers(0, case.N, 12)])) for h in range(H)])
+    _v2_check(case, rows=rows.astype(np.int64))
+
+
+def test_prefill_v2_equals_v1_entry_on_expanded_tensors():
+    # The V2 entry point is the V1 kernel with head strides; on materialised
+    # per-pair tensors both entries give bit-identical results.
+    for D in (64, 128):
+        case = W.V2PrefillCase("v2_vs_v1_d%d" % D, "bf16", B=2, Hq=8, Hkv=2, N=333, D=D, layer=3,
+                               seed=41 + D)
+        say("v2 vs v1 entry D=%d" % D)
+        inp = W.make_prefill_v2(case, device=DEV)
+        lam = gpu_lambda(inp, case.layer)
+        a = api.diffattn_prefill_v2(inp["q"], inp["k"], inp["v"], lam)
+        q1, q2, k1, k2, v = _v2_pair_tensors(inp, case)
+        b = api.diffattn_prefill(q1, q2, k1, k2, v, lam, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Unfused two-pass path: plain attention twice, then the combine pass
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dv,N,causal", [(128, 300, True), (64, 200, False), (128, 64, False)])
+def test_attention_single_map(dv, N, causal):
+    case = W.PrefillCase("attn_dv%d_n%d" % (dv, N), "bf16", B=2, H=3, N=N, d=64, dv=dv, layer=1,
+                         rmsnorm=False, seed=4000 + N, causal=causal)
+    say("single-map attention %s causal=%s" % (case.name, causal))
+    inp = W.make_prefill(case, device=DEV)
+    q1, k1 = inp["q"][..., :64], inp["k"][..., :64]
+    out = api.diffattn_attention(q1, k1, inp["v"], causal=causal)
+    torch.cuda.synchronize()
+    # lambda = 0 turns the oracle's difference into A1 V.
+    ref = run_prefill_oracle(case, inp, np.zeros(case.H, dtype=np.float32))
+    compare(out.cpu().numpy(), ref, "bf16", case.name)
+
+
+def test_unfused_two_pass_matches_oracle_and_fused():
+    case = W.scaled_prefill(W.V1_NORM, B=2, H=4, N=700)
+    say("unfused two-pass %s" % case.name)
+    inp = W.make_prefill(case, device=DEV)
+    lam = gpu_lambda(inp, case.layer)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    scale = 1.0 - api.diffattn_lambda_init(case.layer)
+    o1 = api.diffattn_attention(q[..., :64], k[..., :64], v)
+    o2 = api.diffattn_attention(q[..., 64:], k[..., 64:], v)
+    out = api.diffattn_combine(o1, o2, lam, rmsnorm=True, eps=case.eps, norm_scale=scale)
+    fused = run_prefill_gpu(case, inp, lam)
+    torch.cuda.synchronize()
+    ref = run_prefill_oracle(case, inp, lam.cpu().numpy())
+    compare(out.cpu().numpy(), ref, "bf16", case.name + " unfused")
+    compare(out.cpu().numpy(), fused.cpu().numpy().astype(np.float64), "bf16",
+            case.name + " unfused vs fused")
+
+
+# ---------------------------------------------------------------------------
 # bf16 prefill invariants
 # ---------------------------------------------------------------------------
 
@@ -296,3 +397,76 @@ def test_decode_v2_workload_full():
     # B=32, Hq=32 (16 pairs), Hkv=8, D=128, lengths uniform in [4096, 65536].
     say("decode %s (all outputs)" % W.V2_DECODE.name)
     _decode_check(W.V2_DECODE)
+
+
+# ---------------------------------------------------------------------------
+# V1-layout decode: half-width maps, value cache read once, RMS norm
+# ---------------------------------------------------------------------------
+
+def _decode_v1_oracle(inp, case, lam, rows_of=None, norm_weight=None):
+    """Oracle by definition: the decode query of sequence b is the last row of
+    a causal prefill over its L_b cached positions (test-side marshalling)."""
+    q, kc, vc = (inp[x].cpu() for x in ("q", "k_cache", "v_cache"))
+    lens = inp["seq_lens"].cpu().tolist()
+    d = case.d
+    out = np.zeros((case.B, case.H, case.dv))
+    for b in range(case.B):
+        L = int(lens[b])
+        q1 = torch.zeros((1, case.H, L, d), dtype=q.dtype)
+        q2 = torch.zeros((1, case.H, L, d), dtype=q.dtype)
+        q1[0, :, L - 1] = q[b, :, :d]
+        q2[0, :, L - 1] = q[b, :, d:]
+        k1 = kc[b, :, :L, :d].unsqueeze(0).contiguous()
+        k2 = kc[b, :, :L, d:].unsqueeze(0).contiguous()
+        v = vc[b, :, :L].unsqueeze(0).contiguous()
+        rows = np.array([h * L + L - 1 for h in range(case.H)], dtype=np.int64)
+        out[b] = oracle.prefill(q1, q2, k1, k2, v, lam, causal=True, rmsnorm=case.rmsnorm,
+                                eps=case.eps, norm_scale=(1.0 - oracle.lambda_init(case.layer))
+                                if case.rmsnorm else 1.0, norm_weight=norm_weight, rows=rows)
+    return out
+
+
+def _decode_v1_run(case, inp, lam, norm_weight=None):
+    return api.diffattn_decode_v1(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam,
+                                  rmsnorm=case.rmsnorm, eps=case.eps,
+                                  norm_scale=(1.0 - api.diffattn_lambda_init(case.layer))
+                                  if case.rmsnorm else 1.0, norm_weight=norm_weight)
+
+
+@pytest.mark.parametrize("lens,rms", [([1, 2, 31, 33], True), ([1023, 1024, 1025, 3000], True),
+                                      ([4096, 777, 64, 2049], False)])
+def test_decode_v1_ragged_lengths(lens, rms):
+    case = W.V1DecodeCase("v1_decode_small_%d" % lens[-1], B=len(lens), H=3, d=64, dv=128,
+                          Lmin=1, Lmax=max(lens), layer=5, seed=900 + lens[-1], rmsnorm=rms)
+    say("v1 decode %s lens=%s rms=%s" % (case.name, lens, rms))
+    inp = W.make_decode_v1(case, device=DEV)
+    inp["seq_lens"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    lam = gpu_lambda(inp, case.layer)
+    got = _decode_v1_run(case, inp, lam).cpu().numpy()
+    ref = _decode_v1_oracle(inp, case, lam.cpu().numpy())
+    compare(got, ref, "bf16", case.name)
+
+
+def test_decode_v1_norm_weight_and_bad_length():
+    case = W.V1DecodeCase("v1_decode_weighted", B=3, H=2, d=64, dv=128, Lmin=100, Lmax=600,
+                          layer=8, seed=31)
+    say("v1 decode with a norm weight and an invalid length")
+    inp = W.make_decode_v1(case, device=DEV)
+    lam = gpu_lambda(inp, case.layer)
+    w = (1.0 + 0.5 * torch.randn(128, generator=torch.Generator().manual_seed(9))).float()
+    got = _decode_v1_run(case, inp, lam, norm_weight=w.to(DEV)).cpu().numpy()
+    ref = _decode_v1_oracle(inp, case, lam.cpu().numpy(), norm_weight=w)
+    compare(got, ref, "bf16", case.name)
+    inp["seq_lens"][1] = 0
+    got = _decode_v1_run(case, inp, lam).cpu().numpy()
+    assert np.all(got[1] == 0.0)
+
+
+def test_decode_v1_workload_scaled():
+    case = W.scaled_decode(W.V1_DECODE, B=4)
+    say("v1 decode %s (B=4, full lengths)" % case.name)
+    inp = W.make_decode_v1(case, device=DEV)
+    lam = gpu_lambda(inp, case.layer)
+    got = _decode_v1_run(case, inp, lam).cpu().numpy()
+    ref = _decode_v1_oracle(inp, case, lam.cpu().numpy())
+    compare(got, ref, "bf16", case.name)
