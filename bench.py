@@ -338,6 +338,38 @@ def measure_extras(dev, reps):
                            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     del inp, ws, out
     torch.cuda.empty_cache()
+
+    # Signal-to-noise of the last query towards a planted needle, plain vs
+    # differential, as the context grows (kernel run with probe values).
+    from differential_attention_prefill_amd import snr
+    # The needle key is scaled so that its score sits 10 above zero (the mean
+    # noise score) in every head, a fixed signal strength across lengths.
+    sweep = []
+    for n in (1024, 4096, 16384, 65536, 262144):
+        c = W.scaled_prefill(W.NEEDLE_32K, N=n, H=16, dv=64, needle_score=10.0)
+        print("# extras: noise floor N=%d" % n, file=sys.stderr, flush=True)
+        inp = W.make_prefill(c, device=dev)
+        lam = api.diffattn_lambda(*(inp[x].contiguous() for x in ("lq1", "lk1", "lq2", "lk2")),
+                                  layer=c.layer)
+        r = snr.noise_sweep_point(inp["q"], inp["k"], lam, inp["needles"][:, 0])
+        pt = {"N": n, "heads": c.H}
+        for key in ("plain_signal", "plain_noise", "diff_signal", "diff_noise"):
+            pt[key + "_mean"] = round(float(r[key].mean()), 5)
+        for key in ("plain_snr", "diff_snr"):
+            pt[key + "_median"] = round(float(r[key].median()), 2)
+        sweep.append(pt)
+        del inp
+    extras["snr_sweep"] = sweep
+    c = W.scaled_prefill(W.MULTI_NEEDLE_64K, H=4, dv=64)
+    inp = W.make_prefill(c, device=dev)
+    lam = api.diffattn_lambda(*(inp[x].contiguous() for x in ("lq1", "lk1", "lq2", "lk2")),
+                              layer=c.layer)
+    m = snr.needle_mass(inp["q"], inp["k"], lam, inp["needles"])
+    extras["needle_mass_64k"] = {"workload": c.name, "needles": c.n_needles, "heads": c.H,
+                                 "plain_mean": round(float(m["plain"].mean()), 5),
+                                 "diff_mean": round(float(m["diff"].mean()), 5)}
+    del inp
+    torch.cuda.empty_cache()
     return extras
 
 

@@ -45,6 +45,11 @@ class PrefillCase:
     eps: float = 1e-5
     needle: str = "none"   # "none" | "last_query" | "mean_query"
     n_needles: int = 0
+    needle_scale: float = 5.0   # needle key = needle_scale x (probing query half)
+    # If set, "last_query" needles are instead scaled so that the first-map
+    # score q1 . k1 / sqrt(d) of the probing query equals this value in every
+    # head (a controlled signal strength for noise-floor sweeps).
+    needle_score: Optional[float] = None
 
     @property
     def torch_dtype(self):
@@ -182,12 +187,18 @@ def make_prefill(case: PrefillCase, device="cpu") -> dict:
     lam = [_normal((H, d), g, device, torch.float32, std=0.1) for _ in range(4)]
     needles = torch.zeros((H, 0), dtype=torch.int64)
     if case.needle == "last_query":
-        # One position per head whose first-map key is 5x the last query's
-        # first-map half (the strong match of the noise-floor probe).
+        # One position per head whose first-map key is needle_scale x the last
+        # query's first-map half (the strong match of the noise-floor probe;
+        # the pages use 5x).
         pos = torch.randint(0, N - 1, (H,), generator=g, device=device, dtype=torch.int64)
         for h in range(H):
             p = int(pos[h])
-            k[:, h, p, :d] = (q[:, h, N - 1, :d].float() * 5.0).to(dt)
+            qh = q[:, h, N - 1, :d].float()
+            if case.needle_score is None:
+                scale = case.needle_scale
+            else:
+                scale = case.needle_score * (d ** 0.5) / (qh * qh).sum(dim=-1, keepdim=True)
+            k[:, h, p, :d] = (qh * scale).to(dt)
         needles = pos.cpu().reshape(H, 1)
     elif case.needle == "mean_query":
         # n positions shared by every head; first-map key rows = 5x the mean of
@@ -197,7 +208,7 @@ def make_prefill(case: PrefillCase, device="cpu") -> dict:
         for b in range(B):
             for h in range(H):
                 m = q[b, h, :, :d].double().mean(dim=0)
-                k[b, h, pos, :d] = (m * 5.0).to(dt).unsqueeze(0).expand(pos.numel(), d)
+                k[b, h, pos, :d] = (m * case.needle_scale).to(dt).unsqueeze(0).expand(pos.numel(), d)
         needles = pos.cpu().reshape(1, -1).expand(H, -1).contiguous()
     return {"q": q, "k": k, "v": v, "lq1": lam[0], "lk1": lam[1], "lq2": lam[2],
             "lk2": lam[3], "needles": needles}

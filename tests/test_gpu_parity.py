@@ -470,3 +470,50 @@ def test_decode_v1_workload_scaled():
     got = _decode_v1_run(case, inp, lam).cpu().numpy()
     ref = _decode_v1_oracle(inp, case, lam.cpu().numpy())
     compare(got, ref, "bf16", case.name)
+
+
+# ---------------------------------------------------------------------------
+# Signal-to-noise read off the kernel with probe values
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N", [1024, 4096])
+def test_snr_probe_matches_oracle(N):
+    from differential_attention_prefill_amd import snr
+    # A score of 10 keeps the signal weight well inside (0, 1) at these lengths.
+    case = W.scaled_prefill(W.NEEDLE_32K, N=N, H=4, dv=64, needle_score=10.0)
+    say("snr probe %s N=%d" % (case.name, N))
+    inp = W.make_prefill(case, device=DEV)
+    lam = gpu_lambda(inp, case.layer)
+    sig = inp["needles"][:, 0]
+    got = snr.snr_last_query(inp["q"], inp["k"], lam, sig)
+    q, k = inp["q"].cpu(), inp["k"].cpu()
+    q1, q2, k1, k2 = (t.contiguous() for t in (q[..., :64], q[..., 64:], k[..., :64], k[..., 64:]))
+    lam_h = lam.cpu().numpy()
+    for h in range(case.H):
+        a1, a2 = oracle.prefill_weights(q1, q2, k1, k2, 0, h, N - 1)
+        ref = oracle.snr_from_weights(a1, a2, float(lam_h[h]), int(sig[h]), N)
+        for name in ("plain", "diff"):
+            g, r = float(got[name][h]), ref[name]
+            say("  head %d %s: kernel %.4g oracle %.4g" % (h, name, g, r))
+            assert abs(g - r) <= 2e-2 * abs(r), (h, name, g, r)
+
+
+def test_needle_mass_probe_matches_oracle():
+    from differential_attention_prefill_amd import snr
+    case = W.scaled_prefill(W.MULTI_NEEDLE_64K, N=4096, H=3, dv=64)
+    say("needle mass probe %s" % case.name)
+    inp = W.make_prefill(case, device=DEV)
+    lam = gpu_lambda(inp, case.layer)
+    got = snr.needle_mass(inp["q"], inp["k"], lam, inp["needles"])
+    q, k = inp["q"].cpu(), inp["k"].cpu()
+    q1, q2, k1, k2 = (t.contiguous() for t in (q[..., :64], q[..., 64:], k[..., :64], k[..., 64:]))
+    lam_h = lam.cpu().numpy()
+    for h in range(case.H):
+        a1, a2 = oracle.prefill_weights(q1, q2, k1, k2, 0, h, case.N - 1)
+        pos = inp["needles"][h].numpy()
+        w = a1 - float(lam_h[h]) * a2
+        ref = {"plain": a1[pos].sum(), "diff": w[pos].sum() / w.sum()}
+        for name in ("plain", "diff"):
+            g = float(got[name][h])
+            say("  head %d %s: kernel %.5f oracle %.5f" % (h, name, g, ref[name]))
+            assert abs(g - ref[name]) <= 1e-2 * max(abs(ref[name]), 1e-3), (h, name)
