@@ -168,7 +168,13 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                                                                qf[st], s[t], 0, 0, 0);
         }
         if (it + 1 < DEC_ITERS) fetch(it + 1);
-        __syncthreads();
+        // The V^T tile is private to this wave and a wave's LDS accesses are
+        // performed in order, so ordering the stores before the loads below
+        // needs only a wavefront-scope fence, not a workgroup barrier (which
+        // would hold every wave to the slowest one each iteration).
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if (!active) continue;
 
         // Mask positions past the chunk end; online softmax per head.
