@@ -26,10 +26,11 @@
 //  - Keys and values stream through LDS in tiles of 64 keys, three stages
 //    deep, copied by buffer loads that write LDS directly.  Tile t is read
 //    during global phases 4t .. 4t+5; every wave copies the same number of
-//    1 KB blocks of it, one per phase from phase 4t-6 on, into the stage that
+//    1 KB blocks of it, all at the end of phase 4t-6, into the stage that
 //    tile t-3 left, and the barrier ending phase 4t-1 publishes them.  Copies
-//    complete in issue order, so a wave waits for an older tile with a fixed
-//    count of newer copies still in flight.
+//    complete in issue order, so a wave waits for tile t with exactly the
+//    copies of tile t+1 (issued in phase 4t-2) still in flight.  One burst
+//    every four phases keeps the per-phase scalar work to a single test.
 //  - Tile layout, score orientation (S^T = K . Q^T, a lane holds 16 keys of
 //    one query), the key permutation that lets probabilities feed
 //    O^T += V^T . P^T straight from registers, the transpose load of V, and
@@ -230,35 +231,35 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         cpitch[b] = (int)(ld * 2);
     }
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-    auto issue_block = [&](int t, int b) {
-        // Rows past the sequence end read as zeros (their scores are masked).
+    // All CPW blocks of tile t.  Rows past the sequence end read as zeros
+    // (their scores are masked).
+    auto issue_tile = [&](int t) {
         const int rows = min(N - t * TK, TK);
         const unsigned st = lds0 + (unsigned)((t % PP_NSTAGE) * C::STAGE);
 #pragma unroll
         for (int bb = 0; bb < C::CPW; ++bb) {
-            if (bb != b) continue;
             const i32x4 r = make_rsrc((const void*)(cbase[bb] + (unsigned long long)t * cstride[bb]),
                                       rows * cpitch[bb]);
             copy16_to_lds(r, st + (wave + PP_WAVES * bb) * 1024, coff[bb]);
         }
     };
-    // Global phase p issues block (p+6) % 4 of tile (p+6) / 4: a tile's blocks
-    // go out one per phase over phases 4t-6 .. 4t-7+CPW, so no phase carries
-    // a burst of copies.  (Tiles 0 and 1 are issued whole before the loop.)
+    // Global phase 4t-6 issues tile t (t >= 2; tiles 0 and 1 go out before
+    // the loop).  Its stage was last read in phase 4t-7, and the barrier
+    // ending that phase orders the reads before these writes.
     auto phase_issue = [&](int p) {
-        const int t = (p + 6) >> 2, b = (p + 6) & 3;
-        if (t >= 2 && t < ntile && b < C::CPW) issue_block(t, b);
+        if ((p & 3) != 2) return;
+        const int t = (p + 6) >> 2;
+        if (t < ntile) issue_tile(t);
     };
-    // The end of phase 4t-1 waits for tile t.  Tile t+1 then has its first two
-    // blocks in flight (issued at phases 4t-2 and 4t-1); copies complete in
-    // issue order.
+    // The end of phase 4t-1 waits for tile t.  The only newer copies are those
+    // of tile t+1 (phase 4t-2); tile t+2 goes out in phase 4t+2.
     auto phase_wait = [&](int p) {
-        if (((p + 1) & 3) != 0) return;
+        if ((p & 3) != 3) return;
         const int t = (p + 1) >> 2;
-        if (t + 1 < ntile) wait_copies<2>();
+        if (t + 1 < ntile) wait_copies<C::CPW>();
         else wait_copies<0>();
     };
-    static_assert(C::CPW >= 2 && C::CPW <= 4, "copy schedule assumes 2..4 blocks per wave");
+    static_assert(C::CPW >= 1 && C::CPW <= 15, "copies per wave must fit the vmcnt field");
 
     auto stage_of = [&](int j) -> const unsigned char* {
         return smem + ((j >> 1) % PP_NSTAGE) * C::STAGE;
@@ -323,10 +324,13 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         bool any_grow = false;
 #pragma unroll
         for (int m = 0; m < MAPS; ++m) {
-            float mx = max3(s[m][0], s[m][1], s[m][2]);
-#pragma unroll
-            for (int r = 3; r < 15; r += 2) mx = max3(mx, s[m][r], s[m][r + 1]);
-            mx = max3(mx, s[m][15], s[m][15]);
+            // A tree of three-way maxima: short dependency chains.
+            const float a0 = max3(s[m][0], s[m][1], s[m][2]);
+            const float a1 = max3(s[m][3], s[m][4], s[m][5]);
+            const float a2 = max3(s[m][6], s[m][7], s[m][8]);
+            const float a3 = max3(s[m][9], s[m][10], s[m][11]);
+            const float a4 = max3(s[m][12], s[m][13], s[m][14]);
+            const float mx = max3(max3(a0, a1, a2), a3, max3(a4, s[m][15], s[m][15]));
             const f32x2 hm = halves(mx);
             mnew[m] = max3(mref[m], hm[0], hm[1]);
             grow[m] = mnew[m] > mthr[m];
@@ -375,14 +379,12 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // ---- the schedule ------------------------------------------------------
     // Global phase p: group 0 runs M(j) at p = 2j and V(j) at 2j+1, group 1
     // runs M(j) at 2j+1 and V(j) at 2j+2.  Tile t (sub-tiles 2t, 2t+1) is read
-    // in phases 4t .. 4t+5; its blocks are copied in phases 4t-6 .. 4t-3 into
-    // the stage that tile t-3 left after phase 4t-7, and the barrier ending
-    // phase 4t-1 publishes them.
-#pragma unroll
-    for (int b = 0; b < C::CPW; ++b) issue_block(0, b);
+    // in phases 4t .. 4t+5; its blocks are copied at the end of phase 4t-6
+    // into the stage that tile t-3 left after phase 4t-7, and the barrier
+    // ending phase 4t-1 publishes them.
+    issue_tile(0);
     if (ntile > 1) {
-#pragma unroll
-        for (int b = 0; b < C::CPW; ++b) issue_block(1, b);
+        issue_tile(1);
         wait_copies<C::CPW>();
     } else {
         wait_copies<0>();
@@ -391,12 +393,12 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     if (grp) phase_barrier();   // group 1 starts one phase later
     for (int j = 0; j <= nsub; ++j) {
         const int p = 2 * j + grp;
-        phase_issue(p);
         m_phase(j);
+        phase_issue(p);
         phase_wait(p);
         phase_barrier();
-        phase_issue(p + 1);
         v_phase(j);
+        phase_issue(p + 1);
         phase_wait(p + 1);
         phase_barrier();
     }
