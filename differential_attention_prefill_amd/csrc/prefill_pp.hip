@@ -90,6 +90,28 @@ __device__ __forceinline__ void wait_copies() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
 }
 
+// A constant the compiler must rematerialise (one scalar move) at each use
+// instead of hoisting a per-lane copy of every derived address out of the
+// loop: the loop runs at the vector-register limit.
+__device__ __forceinline__ int fresh(int c) {
+    asm volatile("" : "+s"(c));
+    return c;
+}
+
+// Scheduling groups of the pipelined M phase: load units 0 and 1, then for
+// each unit u its matrix products followed by the loads of unit u+2.  Units
+// 0 .. VB-1 are V^T blocks (4 LDS reads, 2*MAPS products), the rest are key
+// k-steps (MAPS reads, MAPS products).
+template <int U, int NU, int VB, int MAPS>
+struct PipeGroups {
+    static __device__ __forceinline__ void run() {
+        __builtin_amdgcn_sched_group_barrier(0x008, U < VB ? 2 * MAPS : MAPS, 0);   // MFMA
+        if constexpr (U + 2 < NU)
+            __builtin_amdgcn_sched_group_barrier(0x100, (U + 2) < VB ? 4 : MAPS, 0);   // LDS read
+        if constexpr (U + 1 < NU) PipeGroups<U + 1, NU, VB, MAPS>::run();
+    }
+};
+
 template <int D, int DV, int MAPS>
 __global__ void __launch_bounds__(PP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
@@ -153,15 +175,14 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     __builtin_amdgcn_s_waitcnt(0);
 
     const float c = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
-    float mref[MAPS];   // reference maxima (raw score units)
-    // Growth threshold mref + TAU/c: a new maximum above it triggers a rescale
-    // (-inf until a row has seen a visible key).
+    float mref[MAPS];   // reference maxima (raw score units; -inf until a row
+                        // has seen a visible key)
+    // A new maximum above mref + TAU/c triggers a rescale.
     const float tau_raw = TAU / c;
-    float mthr[MAPS];
     float lsum[MAPS];   // this lane's share of the normalisers
 #pragma unroll
     for (int m = 0; m < MAPS; ++m) {
-        mref[m] = mthr[m] = -INFINITY;
+        mref[m] = -INFINITY;
         lsum[m] = 0.f;
     }
     f32x16 acc[MAPS][C::VBLK];
@@ -226,9 +247,13 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         const int id = wave + PP_WAVES * b;
         const __bf16* src = id < C::KBLK ? k1 : (id < MAPS * C::KBLK ? k2 : v);
         const int64_t ld = id < MAPS * C::KBLK ? ldk : ldv;
-        cbase[b] = (unsigned long long)(src + (id < MAPS * C::KBLK ? koff : voff));
-        cstride[b] = (unsigned)(TK * ld * 2);
-        cpitch[b] = (int)(ld * 2);
+        // Uniform values: kept in scalar registers.
+        const unsigned long long a64 = (unsigned long long)(src + (id < MAPS * C::KBLK ? koff : voff));
+        const unsigned alo = __builtin_amdgcn_readfirstlane((unsigned)(a64 & 0xffffffffu));
+        const unsigned ahi = __builtin_amdgcn_readfirstlane((unsigned)(a64 >> 32));
+        cbase[b] = ((unsigned long long)ahi << 32) | alo;
+        cstride[b] = __builtin_amdgcn_readfirstlane((unsigned)(TK * ld * 2));
+        cpitch[b] = __builtin_amdgcn_readfirstlane((int)(ld * 2));
     }
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
     // All CPW blocks of tile t.  Rows past the sequence end read as zeros
@@ -265,46 +290,70 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         return smem + ((j >> 1) % PP_NSTAGE) * C::STAGE;
     };
 
-    // M(j): P.V of sub-tile j-1 (both maps share each V^T fragment), then the
-    // scores of sub-tile j for both maps.
+    // M(j), for j <= jmax: P.V of sub-tile j-1 (both maps share each V^T
+    // fragment) and the scores of sub-tile j for both maps, as one software
+    // pipeline over units (the V^T blocks, then the key k-steps) with the
+    // loads two units ahead.  At j = 0 the probabilities are all zero and the
+    // values of sub-tile 0 stand in, adding exact zeros; at j = jmax the
+    // scores come from whatever the stage holds and are never used.  One code
+    // path for every step keeps the accumulators in place.  The derived LDS
+    // offsets are rematerialised per use (fresh) rather than kept per lane.
     auto m_phase = [&](int j) {
-        if (j >= 1 && j - 1 < jmax) {
-            const unsigned char* vs = stage_of(j - 1) + ((j - 1) & 1) * BN * C::VROWB;
-#pragma unroll
-            for (int nb = 0; nb < C::VBLK; ++nb) {
+        if (j > jmax) return;
+        const int jv = j > 0 ? j - 1 : 0;
+        const unsigned char* vs = stage_of(jv) + (jv & 1) * BN * C::VROWB;
+        const unsigned char* ks = stage_of(j) + (j & 1) * BN * C::KROWB;
+        constexpr int NU = C::VBLK + C::KSTEPS;
+        bf16x8 vf[C::VBLK][2];
+        bf16x8 kf[MAPS][C::KSTEPS];
+        auto load_unit = [&](int u) {
+            if (u < C::VBLK) {
 #pragma unroll
                 for (int t2 = 0; t2 < 2; ++t2) {
-                    const unsigned char* vp = vs + (vx ^ (64 * nb)) + t2 * 16 * C::VROWB;
+                    const unsigned char* vp = vs + (u ? (vx ^ fresh(64 * u)) : vx) + t2 * 16 * C::VROWB;
                     const bf16x4 lo = lds_read_tr(vp);
                     const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
-                    const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    vf[u < C::VBLK ? u : 0][t2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            } else {
+                const int st = u - C::VBLK;
+#pragma unroll
+                for (int m = 0; m < MAPS; ++m)
+                    kf[m][st] = __builtin_bit_cast(
+                        bf16x8, load16(ks + m * C::K2_OFF + (st ? (kx ^ fresh(32 * st)) : kx)));
+            }
+        };
+#pragma unroll
+        for (int m = 0; m < MAPS; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
+        load_unit(0);
+        load_unit(1);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if (u < C::VBLK) {
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
                     for (int m = 0; m < MAPS; ++m)
-                        acc[m][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[m][t2], acc[m][nb], 0, 0, 0);
-                }
+                        acc[m][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u][t2], pf[m][t2], acc[m][u], 0, 0, 0);
+            } else {
+                const int st = u - C::VBLK;
+#pragma unroll
+                for (int m = 0; m < MAPS; ++m)
+                    s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m][st], qf[m][st], s[m], 0, 0, 0);
             }
+            if (u + 2 < NU) load_unit(u + 2);
         }
-        if (j < jmax) {
-#pragma unroll
-            for (int m = 0; m < MAPS; ++m)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
-            const unsigned char* ks = stage_of(j) + (j & 1) * BN * C::KROWB;
-#pragma unroll
-            for (int st = 0; st < C::KSTEPS; ++st) {
-#pragma unroll
-                for (int m = 0; m < MAPS; ++m) {
-                    const bf16x8 kf = __builtin_bit_cast(bf16x8, load16(ks + m * C::K2_OFF + (kx ^ (32 * st))));
-                    s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[m][st], s[m], 0, 0, 0);
-                }
-            }
-        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        PipeGroups<0, NU, C::VBLK, MAPS>::run();
     };
 
     // V(j): both online softmaxes of sub-tile j -> probabilities for M(j+1).
     auto v_phase = [&](int j) {
         if (j >= jmax) return;
-        const int kb = j * BN;
+        const int kb = fresh(j * BN);
         // Rare (diagonal / last sub-tile), uniform: a real branch.
         if (__builtin_expect((kb + BN > N) || (causal && kb + BN - 1 > wrow0), 0)) {
             // Register r holds key kb + key_of_reg(r) + 8*half, visible iff
@@ -333,7 +382,7 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             const float mx = max3(max3(a0, a1, a2), a3, max3(a4, s[m][15], s[m][15]));
             const f32x2 hm = halves(mx);
             mnew[m] = max3(mref[m], hm[0], hm[1]);
-            grow[m] = mnew[m] > mthr[m];
+            grow[m] = mnew[m] > mref[m] + tau_raw;
             any_grow = any_grow | grow[m];
         }
         // Rare: one uniform branch for both maps keeps the common path in one block.
@@ -346,7 +395,6 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                     // all-zero accumulator.
                     const float alpha = grow[m] ? __builtin_amdgcn_exp2f((mref[m] - mnew[m]) * c) : 1.f;
                     mref[m] = grow[m] ? mnew[m] : mref[m];
-                    mthr[m] = mref[m] + tau_raw;
                     lsum[m] *= alpha;
 #pragma unroll
                     for (int nb = 0; nb < C::VBLK; ++nb)
