@@ -439,17 +439,22 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     }
     phase_barrier();            // tile 0 visible
     if (grp) phase_barrier();   // group 1 starts one phase later
+    // The wave in its matrix phase takes issue priority over the one in its
+    // softmax phase on the same SIMD, so the matrix core is fed first.
     for (int j = 0; j <= nsub; ++j) {
         const int p = 2 * j + grp;
+        __builtin_amdgcn_s_setprio(1);
         m_phase(j);
         phase_issue(p);
         phase_wait(p);
         phase_barrier();
+        __builtin_amdgcn_s_setprio(0);
         v_phase(j);
         phase_issue(p + 1);
         phase_wait(p + 1);
         phase_barrier();
     }
+    __builtin_amdgcn_s_setprio(0);
     if (!grp) phase_barrier();  // matches group 1's extra barrier
 
     // ---- epilogue: combine the maps with lambda, optional RMS norm ----------
