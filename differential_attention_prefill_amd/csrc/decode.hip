@@ -8,9 +8,13 @@
 // query heads of a group; part 二 Step 2 for the operator).
 //
 // The cache is read exactly once, which makes the kernel HBM-bound:
-//  - split kernel: grid (split, KV head, sequence).  A workgroup streams one
-//    chunk of DEC_CHUNK positions of K_g and V_g for ALL Hq/Hkv query heads of
-//    the group (both heads of every pair).  Each of its 4 waves takes every
+//  - split kernel: persistent, about two workgroups per CU.  The work items
+//    are the (sequence, KV head, chunk of DEC_CHUNK positions) triples that
+//    hold keys; every workgroup enumerates them from the lengths in the same
+//    order and takes every gridDim.x-th one, so the launch costs the same for
+//    any length mix (a grid over max_len would dispatch mostly empty
+//    workgroups).  One item streams its chunk of K_g and V_g for ALL Hq/Hkv
+//    query heads of the group (both heads of every pair).  Each of its 4 waves takes every
 //    4th 32-key tile of the chunk.  Scores come from v_mfma_f32_16x16x32_bf16
 //    as S^T = K . Q^T (keys x query heads, the 16 columns padded with zero
 //    heads); probabilities go from registers into O^T += V^T . P^T with V^T
@@ -43,7 +47,7 @@ constexpr int DEC_D = 128;             // head width
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
 constexpr int DEC_TILE = 32;           // keys per wave iteration
-constexpr int DEC_CHUNK = 1024;        // keys per split (workgroup)
+constexpr int DEC_CHUNK = 2048;        // keys per work item (one split)
 constexpr int DEC_ITERS = DEC_CHUNK / (DEC_TILE * DEC_WAVES);
 constexpr int DEC_GROUP_MAX = 16;      // query heads per KV head that fit the MFMA columns
 constexpr int DEC_VROW = DEC_TILE * 2 + 16;     // bytes per channel row of V^T (+pad)
@@ -60,18 +64,9 @@ __device__ __forceinline__ int slot_key(int rho, int t) { return (rho >> 2) * 8 
 
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
-                    const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens, int Hq,
-                    int Hkv, int max_len, int max_splits, float* __restrict__ ws, int qhalf,
-                    float c) {
-    const int split = blockIdx.x;
-    const int g = blockIdx.y;
-    const int b = blockIdx.z;
-    const int L = seq_lens[b];
-    if (L < 1 || L > max_len) return;          // the merge kernel writes zeros
-    const int c0 = split * DEC_CHUNK;
-    if (c0 >= L) return;                        // whole workgroup exits together
-    const int cend = min(L, c0 + DEC_CHUNK);
-
+                    const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens, int B,
+                    int Hq, int Hkv, int max_len, int max_splits, float* __restrict__ ws,
+                    int qhalf, float c) {
     // Per-wave V^T tiles during the stream; reused as the wave-merge buffer.
     __shared__ __attribute__((aligned(16))) unsigned char lds[DEC_WAVES * DEC_VBYTES];
     __shared__ float merge_m[DEC_WAVES][DEC_GROUP_MAX];
@@ -88,176 +83,202 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
     const int G = Hq / Hkv;         // query heads in this KV group
     const bool col_ok = col < G;
 
-    const int64_t kv0 = ((int64_t)b * Hkv + g) * max_len;   // row of position 0
-    // c = log2(e) / sqrt(dot length), from the host.
-
-    // Q^T fragments: lane (col, grp) holds q[head col][s*32 + grp*8 .. +8].
-    // V1 (qhalf > 0): both columns read the packed row [q1 | q2] of head g and
-    // keep only their own half.
-    bf16x8 qf[4];
-    {
-        const __bf16* qr = qhalf > 0 ? q + ((int64_t)b * Hkv + g) * DEC_D + grp * 8
-                                     : q + ((int64_t)b * Hq + g * G + (col_ok ? col : 0)) * DEC_D + grp * 8;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const bool mine = qhalf > 0 ? ((s * 32 + grp * 8 < qhalf) == (col == 0)) : true;
-            uint4 v = col_ok && mine ? ld16(qr + s * 32) : make_uint4(0, 0, 0, 0);
-            qf[s] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-
-    float mref = -INFINITY, lsum = 0.f;
-    f32x4 acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Prefetch registers: K fragments in A-operand order, V rows for the
-    // transposed LDS store (lane = 4 items of (key pair, 8-channel chunk)).
-    uint4 kreg[2][4];
-    uint4 vreg[4][2];
-    auto fetch = [&](int it) {
-        const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int key = kb + slot_key(col, t);
-            const bool ok = key < cend;
-            const __bf16* src = kc + (kv0 + (ok ? key : 0)) * DEC_D + grp * 8;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) kreg[t][s] = ok ? ld16(src + s * 32) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int item = lane + 64 * i;
-            const int kp = item >> 4, ch = item & 15;
-            const int key = kb + 2 * kp;
-            vreg[i][0] = key < cend ? ld16(vc + (kv0 + key) * DEC_D + ch * 8) : make_uint4(0, 0, 0, 0);
-            vreg[i][1] = key + 1 < cend ? ld16(vc + (kv0 + key + 1) * DEC_D + ch * 8)
-                                        : make_uint4(0, 0, 0, 0);
-        }
+    // Chunks of sequence b (0 for an invalid length: the merge kernel then
+    // writes zeros).  Items are numbered sequence by sequence, KV head by KV
+    // head, chunk by chunk.
+    auto nchunks = [&](int bb) -> int {
+        const int Lb = seq_lens[bb];
+        return (Lb < 1 || Lb > max_len) ? 0 : (Lb + DEC_CHUNK - 1) / DEC_CHUNK;
     };
+    int total = 0;
+    for (int bb = 0; bb < B; ++bb) total += nchunks(bb) * Hkv;
+    int b = 0, base = 0, nb = B > 0 ? nchunks(0) : 0;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        // Items only grow, so the sequence pointer only moves forward; item <
+        // total keeps it below B.
+        while (item >= base + nb * Hkv) {
+            base += nb * Hkv;
+            ++b;
+            nb = nchunks(b);
+        }
+        const int g = (item - base) / nb;
+        const int split = (item - base) % nb;
+        const int L = seq_lens[b];
+        const int c0 = split * DEC_CHUNK;
+        const int cend = min(L, c0 + DEC_CHUNK);
 
-    fetch(0);
-    for (int it = 0; it < DEC_ITERS; ++it) {
-        const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
-        const bool active = kb < cend;
-        // Only this wave touches its tile, and a wave's LDS operations complete
-        // in program order, so last iteration's reads precede these writes.
-        unsigned char* vt = lds + wave * DEC_VBYTES;
-        // V tile -> LDS, transposed to [channel][key].
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int item = lane + 64 * i;
-            const int kp = item >> 4, ch = item & 15;
-            const unsigned aw[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-            const unsigned bw[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const unsigned lo = (e & 1) ? (aw[e >> 1] >> 16) : (aw[e >> 1] & 0xffffu);
-                const unsigned hi = (e & 1) ? (bw[e >> 1] & 0xffff0000u) : (bw[e >> 1] << 16);
-                *reinterpret_cast<unsigned*>(vt + (ch * 8 + e) * DEC_VROW + kp * 4) = lo | hi;
+        const int64_t kv0 = ((int64_t)b * Hkv + g) * max_len;   // row of position 0
+        // c = log2(e) / sqrt(dot length), from the host.
+
+        // Q^T fragments: lane (col, grp) holds q[head col][s*32 + grp*8 .. +8].
+        // V1 (qhalf > 0): both columns read the packed row [q1 | q2] of head g and
+        // keep only their own half.
+        bf16x8 qf[4];
+        {
+            const __bf16* qr = qhalf > 0 ? q + ((int64_t)b * Hkv + g) * DEC_D + grp * 8
+                                         : q + ((int64_t)b * Hq + g * G + (col_ok ? col : 0)) * DEC_D + grp * 8;
+    #pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bool mine = qhalf > 0 ? ((s * 32 + grp * 8 < qhalf) == (col == 0)) : true;
+                uint4 v = col_ok && mine ? ld16(qr + s * 32) : make_uint4(0, 0, 0, 0);
+                qf[s] = __builtin_bit_cast(bf16x8, v);
             }
         }
-        // S^T = K . Q^T for the two 16-key halves of the tile.
-        f32x4 s[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[t][st]),
-                                                               qf[st], s[t], 0, 0, 0);
-        }
-        if (it + 1 < DEC_ITERS) fetch(it + 1);
-        // The V^T tile is private to this wave and a wave's LDS accesses are
-        // performed in order, so ordering the stores before the loads below
-        // needs only a wavefront-scope fence, not a workgroup barrier (which
-        // would hold every wave to the slowest one each iteration).
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (!active) continue;
 
-        // Mask positions past the chunk end; online softmax per head.
-        float sv[8];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kb + slot_key(grp * 4 + r, t);
-                sv[t * 4 + r] = key < cend ? s[t][r] : -INFINITY;
+        float mref = -INFINITY, lsum = 0.f;
+        f32x4 acc[8];
+    #pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // Prefetch registers: K fragments in A-operand order, V rows for the
+        // transposed LDS store (lane = 4 items of (key pair, 8-channel chunk)).
+        uint4 kreg[2][4];
+        uint4 vreg[4][2];
+        auto fetch = [&](int it) {
+            const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
+    #pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int key = kb + slot_key(col, t);
+                const bool ok = key < cend;
+                const __bf16* src = kc + (kv0 + (ok ? key : 0)) * DEC_D + grp * 8;
+    #pragma unroll
+                for (int s = 0; s < 4; ++s) kreg[t][s] = ok ? ld16(src + s * 32) : make_uint4(0, 0, 0, 0);
             }
-        float mx = sv[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mref, mx);
-        const bool grow = mref == -INFINITY || (mnew - mref) * c > DEC_TAU;
-        if (__any(grow)) {
-            const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * c);  // 0 on first use
-            mref = mnew;
-            lsum *= alpha;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] *= alpha;
-        }
-        const float mc = mref * c;
-        bf16x8 pf;
-        float ls = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(sv[e], c, -mc)),
-                        __builtin_amdgcn_exp2f(fmaf(sv[e + 1], c, -mc))};
-            ls += pr[0] + pr[1];
-            bf16x2 pb = __builtin_convertvector(pr, bf16x2);
-            pf[e] = pb[0];
-            pf[e + 1] = pb[1];
-        }
-        lsum += ls;
-        // O^T += V^T . P^T over 8 blocks of 16 channels.
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-            bf16x8 vf = __builtin_bit_cast(bf16x8, ld16(vt + (blk * 16 + col) * DEC_VROW + grp * 16));
-            acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[blk], 0, 0, 0);
-        }
-    }
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int item = lane + 64 * i;
+                const int kp = item >> 4, ch = item & 15;
+                const int key = kb + 2 * kp;
+                vreg[i][0] = key < cend ? ld16(vc + (kv0 + key) * DEC_D + ch * 8) : make_uint4(0, 0, 0, 0);
+                vreg[i][1] = key + 1 < cend ? ld16(vc + (kv0 + key + 1) * DEC_D + ch * 8)
+                                            : make_uint4(0, 0, 0, 0);
+            }
+        };
 
-    // Every wave saw at least one key of the chunk only if its first tile was
-    // inside it; idle waves carry m = -inf, l = 0, O = 0 and merge as nothing.
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    __syncthreads();   // every wave is done reading its V^T tile
-    if (col_ok) {
-        if (grp == 0) {
-            merge_m[wave][col] = mref;
-            merge_l[wave][col] = lsum;
+        fetch(0);
+        for (int it = 0; it < DEC_ITERS; ++it) {
+            const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
+            const bool active = kb < cend;
+            // Only this wave touches its tile, and a wave's LDS operations complete
+            // in program order, so last iteration's reads precede these writes.
+            unsigned char* vt = lds + wave * DEC_VBYTES;
+            // V tile -> LDS, transposed to [channel][key].
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int item = lane + 64 * i;
+                const int kp = item >> 4, ch = item & 15;
+                const unsigned aw[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
+                const unsigned bw[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const unsigned lo = (e & 1) ? (aw[e >> 1] >> 16) : (aw[e >> 1] & 0xffffu);
+                    const unsigned hi = (e & 1) ? (bw[e >> 1] & 0xffff0000u) : (bw[e >> 1] << 16);
+                    *reinterpret_cast<unsigned*>(vt + (ch * 8 + e) * DEC_VROW + kp * 4) = lo | hi;
+                }
+            }
+            // S^T = K . Q^T for the two 16-key halves of the tile.
+            f32x4 s[2];
+    #pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[t][st]),
+                                                                   qf[st], s[t], 0, 0, 0);
+            }
+            if (it + 1 < DEC_ITERS) fetch(it + 1);
+            // The V^T tile is private to this wave and a wave's LDS accesses are
+            // performed in order, so ordering the stores before the loads below
+            // needs only a wavefront-scope fence, not a workgroup barrier (which
+            // would hold every wave to the slowest one each iteration).
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (!active) continue;
+
+            // Mask positions past the chunk end; online softmax per head.
+            float sv[8];
+    #pragma unroll
+            for (int t = 0; t < 2; ++t)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = kb + slot_key(grp * 4 + r, t);
+                    sv[t * 4 + r] = key < cend ? s[t][r] : -INFINITY;
+                }
+            float mx = sv[0];
+    #pragma unroll
+            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(mref, mx);
+            const bool grow = mref == -INFINITY || (mnew - mref) * c > DEC_TAU;
+            if (__any(grow)) {
+                const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * c);  // 0 on first use
+                mref = mnew;
+                lsum *= alpha;
+    #pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+            }
+            const float mc = mref * c;
+            bf16x8 pf;
+            float ls = 0.f;
+    #pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(sv[e], c, -mc)),
+                            __builtin_amdgcn_exp2f(fmaf(sv[e + 1], c, -mc))};
+                ls += pr[0] + pr[1];
+                bf16x2 pb = __builtin_convertvector(pr, bf16x2);
+                pf[e] = pb[0];
+                pf[e + 1] = pb[1];
+            }
+            lsum += ls;
+            // O^T += V^T . P^T over 8 blocks of 16 channels.
+    #pragma unroll
+            for (int blk = 0; blk < 8; ++blk) {
+                bf16x8 vf = __builtin_bit_cast(bf16x8, ld16(vt + (blk * 16 + col) * DEC_VROW + grp * 16));
+                acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[blk], 0, 0, 0);
+            }
         }
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) merge_o[wave][col][blk * 16 + grp * 4 + r] = acc[blk][r];
-    }
-    __syncthreads();
-    // Merge the waves: thread = (head, channel).
-    float* ws_split = ws + (((int64_t)b * Hq + g * G) * max_splits + split) * DEC_STATE;
-    for (int e = tid; e < G * DEC_D; e += DEC_THREADS) {
-        const int hh = e / DEC_D, ch = e % DEC_D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, merge_m[w][hh]);
-        float o = 0.f, l = 0.f;
-#pragma unroll
-        for (int w = 0; w < DEC_WAVES; ++w) {
-            const float mw = merge_m[w][hh];
-            const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mw - M) * c);
-            o = fmaf(merge_o[w][hh][ch], f, o);
-            l = fmaf(merge_l[w][hh], f, l);
+
+        // Every wave saw at least one key of the chunk only if its first tile was
+        // inside it; idle waves carry m = -inf, l = 0, O = 0 and merge as nothing.
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        __syncthreads();   // every wave is done reading its V^T tile
+        if (col_ok) {
+            if (grp == 0) {
+                merge_m[wave][col] = mref;
+                merge_l[wave][col] = lsum;
+            }
+    #pragma unroll
+            for (int blk = 0; blk < 8; ++blk)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) merge_o[wave][col][blk * 16 + grp * 4 + r] = acc[blk][r];
         }
-        float* st = ws_split + (int64_t)hh * max_splits * DEC_STATE;
-        st[ch] = o;
-        if (ch == 0) {
-            st[DEC_D] = M * c;
-            st[DEC_D + 1] = l;
+        __syncthreads();
+        // Merge the waves: thread = (head, channel).
+        float* ws_split = ws + (((int64_t)b * Hq + g * G) * max_splits + split) * DEC_STATE;
+        for (int e = tid; e < G * DEC_D; e += DEC_THREADS) {
+            const int hh = e / DEC_D, ch = e % DEC_D;
+            float M = -INFINITY;
+    #pragma unroll
+            for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, merge_m[w][hh]);
+            float o = 0.f, l = 0.f;
+    #pragma unroll
+            for (int w = 0; w < DEC_WAVES; ++w) {
+                const float mw = merge_m[w][hh];
+                const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mw - M) * c);
+                o = fmaf(merge_o[w][hh][ch], f, o);
+                l = fmaf(merge_l[w][hh], f, l);
+            }
+            float* st = ws_split + (int64_t)hh * max_splits * DEC_STATE;
+            st[ch] = o;
+            if (ch == 0) {
+                st[DEC_D] = M * c;
+                st[DEC_D + 1] = l;
+            }
         }
+        __syncthreads();   // the merge buffer is read before the next item's V^T tiles
     }
 }
 
@@ -340,13 +361,32 @@ size_t decode_workspace_floats(int B, int Hq, int D, int max_len) {
     return (size_t)B * Hq * decode_max_splits(max_len) * DEC_STATE;
 }
 
+// Workgroups of the persistent split kernel: two per CU (its register use
+// allows two per CU), never more than there can be items.
+static int decode_split_grid(int B, int Hkv, int S) {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cus[dev] = n;
+    }
+    const int64_t items = (int64_t)B * Hkv * S;
+    const int64_t want = 2 * (int64_t)cus[dev];
+    return (int)(items < want ? items : want);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (a.D != DEC_D || a.Hq / a.Hkv > DEC_GROUP_MAX) return hipErrorInvalidValue;
     const int S = decode_max_splits(a.max_len);
     const float c = 1.4426950408889634f / sqrtf((float)(a.qhalf > 0 ? a.qhalf : DEC_D));
-    hipLaunchKernelGGL(decode_split_kernel, dim3(S, a.Hkv, a.B), dim3(DEC_THREADS), 0, stream,
-                       (const __bf16*)a.q, (const __bf16*)a.k_cache, (const __bf16*)a.v_cache,
-                       a.seq_lens, a.Hq, a.Hkv, a.max_len, S, a.workspace, a.qhalf, c);
+    const int grid = decode_split_grid(a.B, a.Hkv, S);
+    if (grid > 0)
+        hipLaunchKernelGGL(decode_split_kernel, dim3(grid), dim3(DEC_THREADS), 0, stream,
+                           (const __bf16*)a.q, (const __bf16*)a.k_cache, (const __bf16*)a.v_cache,
+                           a.seq_lens, a.B, a.Hq, a.Hkv, a.max_len, S, a.workspace, a.qhalf, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq / 2, a.B), dim3(MERGE_THREADS), 0, stream,
