@@ -354,7 +354,8 @@ def _decode_check(case, fill_unused=None):
     return compare(got, ref, "bf16", case.name)
 
 
-@pytest.mark.parametrize("lens", [[1, 2, 31, 33], [1023, 1024, 1025, 3000], [4096, 777, 4095, 64]])
+@pytest.mark.parametrize("lens", [[1, 2, 31, 33], [1023, 1024, 1025, 3000], [4096, 777, 4095, 64],
+                                  [2047, 2048, 2049, 4097]])
 def test_decode_ragged_lengths(lens):
     case = W.DecodeCase("decode_small_%d" % lens[0], B=len(lens), Hq=8, Hkv=2, D=128,
                         Lmin=1, Lmax=max(lens), layer=2, seed=sum(lens))
@@ -391,6 +392,30 @@ def test_decode_invalid_device_length_gives_zeros():
     ref = oracle.decode(inp["q"][:1].cpu(), inp["k_cache"][:1].cpu(), inp["v_cache"][:1].cpu(),
                         np.array([100], np.int32), lam.cpu().numpy())
     compare(out[:1].cpu().numpy(), ref, "bf16", "decode valid row")
+
+
+def test_decode_many_items_with_invalid_lengths():
+    # More (sequence, KV head, chunk) items than workgroups, so every
+    # workgroup strides over several, with out-of-range lengths in between.
+    B, max_len = 64, 6144
+    case = W.DecodeCase("decode_items", B=B, Hq=16, Hkv=8, D=128, Lmin=1, Lmax=max_len, layer=3,
+                        seed=77)
+    say("decode %d sequences, several chunks each, invalid lengths interleaved" % B)
+    inp = W.make_decode(case, device=DEV)
+    lens = torch.randint(1, max_len + 1, (B,), generator=torch.Generator().manual_seed(11),
+                         dtype=torch.int32)
+    bad = [3, 17, 18, 40, 63]
+    for i, v in zip(bad, [0, -5, max_len + 1, 0, max_len + 100]):
+        lens[i] = v
+    inp["seq_lens"] = lens.to(DEV)
+    lam = gpu_lambda(inp, case.layer)
+    out = api.diffattn_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[bad]).item() == 0
+    good = [b for b in range(B) if b not in bad]
+    ref = oracle.decode(inp["q"][good].cpu(), inp["k_cache"][good].cpu(), inp["v_cache"][good].cpu(),
+                        lens[good].numpy(), lam.cpu().numpy())
+    compare(out[good].cpu().numpy(), ref, "bf16", case.name)
 
 
 def test_decode_v2_workload_full():
@@ -434,7 +459,7 @@ def _decode_v1_run(case, inp, lam, norm_weight=None):
 
 
 @pytest.mark.parametrize("lens,rms", [([1, 2, 31, 33], True), ([1023, 1024, 1025, 3000], True),
-                                      ([4096, 777, 64, 2049], False)])
+                                      ([4096, 777, 64, 2049], False), ([2047, 2048, 6000, 4097], True)])
 def test_decode_v1_ragged_lengths(lens, rms):
     case = W.V1DecodeCase("v1_decode_small_%d" % lens[-1], B=len(lens), H=3, d=64, dv=128,
                           Lmin=1, Lmax=max(lens), layer=5, seed=900 + lens[-1], rmsnorm=rms)
