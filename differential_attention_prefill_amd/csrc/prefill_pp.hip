@@ -25,12 +25,13 @@
 //    causal extent and stay balanced.
 //  - Keys and values stream through LDS in tiles of 64 keys, three stages
 //    deep, copied by buffer loads that write LDS directly.  Tile t is read
-//    during global phases 4t .. 4t+5; every wave copies the same number of
-//    1 KB blocks of it, all at the end of phase 4t-6, into the stage that
-//    tile t-3 left, and the barrier ending phase 4t-1 publishes them.  Copies
-//    complete in issue order, so a wave waits for tile t with exactly the
-//    copies of tile t+1 (issued in phase 4t-2) still in flight.  One burst
-//    every four phases keeps the per-phase scalar work to a single test.
+//    by the M phases of steps 2t .. 2t+2.  Every wave copies the same number
+//    of 1 KB blocks of it, in one burst at the end of its M phase of step
+//    2t-3 (global phase 4t-6 or 4t-5), into the stage that tile t-3 left
+//    after phase 4t-7, and waits for it at the end of its M phase of step
+//    2t-1 with exactly the copies of tile t+1, issued just before, still in
+//    flight (copies complete in issue order); the barrier ending phase 4t-1
+//    publishes the tile.  The softmax phase carries no copy work.
 //  - Tile layout, score orientation (S^T = K . Q^T, a lane holds 16 keys of
 //    one query), the key permutation that lets probabilities feed
 //    O^T += V^T . P^T straight from registers, the transpose load of V, and
@@ -268,22 +269,6 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             copy16_to_lds(r, st + (wave + PP_WAVES * bb) * 1024, coff[bb]);
         }
     };
-    // Global phase 4t-6 issues tile t (t >= 2; tiles 0 and 1 go out before
-    // the loop).  Its stage was last read in phase 4t-7, and the barrier
-    // ending that phase orders the reads before these writes.
-    auto phase_issue = [&](int p) {
-        if ((p & 3) != 2) return;
-        const int t = (p + 6) >> 2;
-        if (t < ntile) issue_tile(t);
-    };
-    // The end of phase 4t-1 waits for tile t.  The only newer copies are those
-    // of tile t+1 (phase 4t-2); tile t+2 goes out in phase 4t+2.
-    auto phase_wait = [&](int p) {
-        if ((p & 3) != 3) return;
-        const int t = (p + 1) >> 2;
-        if (t + 1 < ntile) wait_copies<C::CPW>();
-        else wait_copies<0>();
-    };
     static_assert(C::CPW >= 1 && C::CPW <= 15, "copies per wave must fit the vmcnt field");
 
     auto stage_of = [&](int j) -> const unsigned char* {
@@ -427,9 +412,12 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // ---- the schedule ------------------------------------------------------
     // Global phase p: group 0 runs M(j) at p = 2j and V(j) at 2j+1, group 1
     // runs M(j) at 2j+1 and V(j) at 2j+2.  Tile t (sub-tiles 2t, 2t+1) is read
-    // in phases 4t .. 4t+5; its blocks are copied at the end of phase 4t-6
-    // into the stage that tile t-3 left after phase 4t-7, and the barrier
-    // ending phase 4t-1 publishes them.
+    // by M(2t) .. M(2t+2), phases 4t .. 4t+5.  M(2t-3) copies it into the
+    // stage tile t-3 left after phase 4t-7; M(2t-1) waits for it, and the
+    // barrier ending phase 4t-1 publishes it.  (Checked by a CPU simulation of
+    // both groups over every key extent up to 19200 and at 32k/64k: each
+    // copy issued once into a free stage, complete and published before its
+    // first read, none in flight at the end.)
     issue_tile(0);
     if (ntile > 1) {
         issue_tile(1);
@@ -442,16 +430,19 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // The wave in its matrix phase takes issue priority over the one in its
     // softmax phase on the same SIMD, so the matrix core is fed first.
     for (int j = 0; j <= nsub; ++j) {
-        const int p = 2 * j + grp;
         __builtin_amdgcn_s_setprio(1);
         m_phase(j);
-        phase_issue(p);
-        phase_wait(p);
+        if (j & 1) {
+            // Copy tile (j+3)/2, then wait for tile (j+1)/2 with only the
+            // copies just issued still in flight.
+            const int ti = (j + 3) >> 1, tw = (j + 1) >> 1;
+            if (ti < ntile) issue_tile(ti);
+            if (tw + 1 < ntile) wait_copies<C::CPW>();
+            else wait_copies<0>();
+        }
         phase_barrier();
         __builtin_amdgcn_s_setprio(0);
         v_phase(j);
-        phase_issue(p + 1);
-        phase_wait(p + 1);
         phase_barrier();
     }
     __builtin_amdgcn_s_setprio(0);
