@@ -414,10 +414,10 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // runs M(j) at 2j+1 and V(j) at 2j+2.  Tile t (sub-tiles 2t, 2t+1) is read
     // by M(2t) .. M(2t+2), phases 4t .. 4t+5.  M(2t-3) copies it into the
     // stage tile t-3 left after phase 4t-7; M(2t-1) waits for it, and the
-    // barrier ending phase 4t-1 publishes it.  (Checked by a CPU simulation of
-    // both groups over every key extent up to 19200 and at 32k/64k: each
-    // copy issued once into a free stage, complete and published before its
-    // first read, none in flight at the end.)
+    // barrier ending phase 4t-1 publishes it.  (tests/test_copy_schedule.py
+    // models both groups over every key extent up to 2560 and at 4k/32k/64k:
+    // each copy issued once into a free stage, complete and published before
+    // its first read, none in flight at the end.)
     issue_tile(0);
     if (ntile > 1) {
         issue_tile(1);
