@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 
-SOURCES = ["api.cpp", "lambda.hip", "prefill_f32.hip", "prefill_bf16.hip", "prefill_pp.hip", "combine.hip", "decode.hip"]
+SOURCES = ["api.cpp", "lambda.hip", "prefill_f32.hip", "prefill_pp.hip", "combine.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -27,7 +27,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 # The fused prefill runs with the IEEE mode bit off (its row maxima then need
 # no NaN-quieting instructions); scores there are never NaN.
-EXTRA_FLAGS = {src: ["-fno-honor-nans", "-mno-amdgpu-ieee"] for src in ("prefill_bf16.hip", "prefill_pp.hip")}
+EXTRA_FLAGS = {"prefill_pp.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _compile(src: str) -> str:

@@ -59,9 +59,6 @@ hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, c
 
 bool prefill_bf16_supported(int d, int dv);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
-// Ping-pong schedule (d <= 64); launch_prefill_bf16 dispatches to it.
-bool prefill_pp_supported(int d, int dv);
-hipError_t launch_prefill_pp(const PrefillArgs& a, hipStream_t stream);
 // Single-map softmax attention on the same schedule (q1, k1, v; out = A V).
 bool attention_pp_supported(int d, int dv);
 hipError_t launch_attention_pp(const PrefillArgs& a, hipStream_t stream);

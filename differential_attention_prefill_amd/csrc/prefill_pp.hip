@@ -1,5 +1,6 @@
-// Fused differential-attention prefill, ping-pong schedule (bf16 in, fp32
-// accumulate; d <= 64).
+// Fused differential-attention prefill on gfx950 matrix cores, ping-pong
+// schedules (bf16 in, fp32 accumulate): both maps per wave for d <= 64, one
+// map per wave (map-split) for d = 128.
 //
 // Per head (b,h) and query row i:
 //     A1 = softmax(q1_i K1^T / sqrt d),   A2 = softmax(q2_i K2^T / sqrt d),
@@ -32,10 +33,18 @@
 //    2t-1 with exactly the copies of tile t+1, issued just before, still in
 //    flight (copies complete in issue order); the barrier ending phase 4t-1
 //    publishes the tile.  The softmax phase carries no copy work.
-//  - Tile layout, score orientation (S^T = K . Q^T, a lane holds 16 keys of
-//    one query), the key permutation that lets probabilities feed
-//    O^T += V^T . P^T straight from registers, the transpose load of V, and
-//    the lazy rescale are those of the other bf16 prefill kernel.
+//  - Scores are formed transposed, S^T = K . Q^T (v_mfma_f32_32x32x16_bf16):
+//    a lane holds 16 keys of ONE query, so each softmax row statistic is a
+//    per-lane quantity plus one exchange with the lane 32 apart.  Keys enter
+//    the A operand with bits 2 and 3 of the row index swapped, which makes
+//    the score registers line up with the B operand of O^T += V^T . P^T: the
+//    probabilities feed the next product straight from registers.  Values
+//    stay token-major in LDS and the V^T operand comes from the gfx950
+//    transpose load (ds_read_b64_tr_b16).  Rows are XOR-swizzled in 16-byte
+//    chunks so fragment reads hit distinct banks.
+//  - Rescaling is lazy: an accumulator is rescaled only when a row maximum
+//    grows by more than 8 (base 2) over the reference it was built on, so
+//    probabilities stay <= 2^8; the result is the same exact quantity.
 //  - Causal: sub-tiles wholly above a row block are skipped (the wave still
 //    takes part in every barrier); only those that straddle the diagonal or
 //    the sequence end are masked.  Heavy query tiles are scheduled first, and
@@ -516,16 +525,358 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-}  // namespace
+// ---------------------------------------------------------------------------
+// Map-split ping-pong (d = 128): 8 waves own 128 rows.  Wave w runs map
+// w >> 2 for row block w & 3; the map-2 waves form the second phase group,
+// one phase behind, so each SIMD holds the two maps of one row block, one in
+// its matrix phase while the other is in its softmax phase.  A wave keeps one
+// map's query fragments and accumulator (d = 128 does not fit both).
+constexpr int PS_WAVES = 8;
+constexpr int PS_THREADS = WAVE * PS_WAVES;
+constexpr int PS_BM = QROWS * 4;
 
-bool prefill_pp_supported(int d, int dv) {
-    return (d == 64 && dv == 128) || (d == 64 && dv == 64) || (d == 32 && dv == 64);
+template <int D, int DV>
+struct PSCfg {
+    static constexpr int KC = D / 8;
+    static constexpr int VC = DV / 8;
+    static constexpr int KROWB = D * 2;
+    static constexpr int VROWB = DV * 2;
+    static constexpr int K2_OFF = TK * KROWB;
+    static constexpr int V_OFF = 2 * TK * KROWB;
+    static constexpr int STAGE = 2 * TK * KROWB + TK * VROWB;
+    static constexpr int KBLK = TK * KROWB / 1024;
+    static constexpr int NCOPY = STAGE / 1024;
+    static constexpr int CPW = NCOPY / PS_WAVES;
+    static constexpr int KRPI = 1024 / KROWB;
+    static constexpr int VRPI = 1024 / VROWB;
+    static constexpr int KSTEPS = D / 16;
+    static constexpr int VBLK = DV / 32;
+    static constexpr int XBYTES = 4 * QROWS * DV * 4;   // map-2 hand-over, 4 row blocks
+    static constexpr int LDS = (PP_NSTAGE * STAGE > XBYTES) ? PP_NSTAGE * STAGE : XBYTES;
+    static_assert(NCOPY % PS_WAVES == 0 && CPW >= 1, "copy schedule");
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int D, int DV>
+__global__ void __launch_bounds__(PS_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
+                   const __bf16* __restrict__ k1, const __bf16* __restrict__ k2,
+                   const __bf16* __restrict__ v, int64_t ldq, int64_t ldk, int64_t ldv,
+                   int BH, int H, int N, int causal, const float* __restrict__ lambda,
+                   int rmsnorm, float eps, float norm_scale,
+                   const float* __restrict__ norm_weight, float* __restrict__ out,
+                   int row_tiles, HeadStrides hs) {
+    using C = PSCfg<D, DV>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int map = grp;
+    const int rb = wave & 3;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    const int bh = blockIdx.x % BH;
+    const int tile = row_tiles - 1 - (int)(blockIdx.x / BH);
+    const int h = bh % H;
+    const int q0 = tile * PS_BM;
+    const int64_t tok0 = (int64_t)bh * N;
+    const int b = bh / H;
+    const int64_t qoff = b * hs.qb + h * hs.qh;
+    const int64_t koff = b * hs.kb + (h / hs.kv_group) * hs.kh;
+    const int64_t voff = b * hs.vb + (h / hs.kv_group) * hs.vh;
+
+    const int wrow0 = q0 + rb * QROWS;
+    const int my_row = wrow0 + col;
+    const int wrow_last = min(wrow0 + QROWS, N) - 1;
+    const int kv_end = causal ? min(N, q0 + PS_BM) : N;
+    const int nsub = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
+    const int ntile = __builtin_amdgcn_readfirstlane((kv_end + TK - 1) / TK);
+    const int jmax = __builtin_amdgcn_readfirstlane(
+        wrow_last < wrow0 ? 0 : (causal ? min(nsub, wrow_last / BN + 1) : nsub));
+
+    bf16x8 qf[C::KSTEPS];
+    {
+        const bool ok = my_row < N;
+        const int64_t off = qoff + (int64_t)(ok ? my_row : 0) * ldq + half * 8;
+        const __bf16* qs = map ? q2 : q1;
+#pragma unroll
+        for (int st = 0; st < C::KSTEPS; ++st)
+            qf[st] = __builtin_bit_cast(bf16x8, ok ? load16(qs + off + st * 16) : make_uint4(0, 0, 0, 0));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    const float c = 1.4426950408889634f / sqrtf((float)D);
+    const float tau_raw = TAU / c;
+    float mref = -INFINITY, lsum = 0.f;
+    f32x16 acc[C::VBLK];
+#pragma unroll
+    for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
+    f32x16 s;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[t][e] = (__bf16)0.f;
+
+    const int krow = kappa(col);
+    const int kx = map * C::K2_OFF + krow * C::KROWB + ((half ^ k_swz<D>(krow)) * 16);
+    const int lg = lane >> 4, gl = lane & 15;
+    const int vrow = (lg >> 1) * 8 + (gl >> 2);
+    const int vx = C::V_OFF + vrow * C::VROWB +
+                   (((2 * (lg & 1) + ((gl & 3) >> 1)) ^ v_swz<DV>(vrow)) * 16) + 8 * (gl & 1);
+
+    int coff[C::CPW];
+    unsigned long long cbase[C::CPW];
+    unsigned cstride[C::CPW];
+    int cpitch[C::CPW];
+#pragma unroll
+    for (int bb = 0; bb < C::CPW; ++bb) {
+        const int id = wave + PS_WAVES * bb;
+        if (id < 2 * C::KBLK) {
+            const int row = (id % C::KBLK) * C::KRPI + lane / C::KC;
+            coff[bb] = row * (int)ldk * 2 + (((lane % C::KC) ^ k_swz<D>(row)) * 16);
+        } else {
+            const int row = (id - 2 * C::KBLK) * C::VRPI + lane / C::VC;
+            coff[bb] = row * (int)ldv * 2 + (((lane % C::VC) ^ v_swz<DV>(row)) * 16);
+        }
+        const __bf16* src = id < C::KBLK ? k1 : (id < 2 * C::KBLK ? k2 : v);
+        const int64_t ld = id < 2 * C::KBLK ? ldk : ldv;
+        const unsigned long long a64 = (unsigned long long)(src + (id < 2 * C::KBLK ? koff : voff));
+        const unsigned alo = __builtin_amdgcn_readfirstlane((unsigned)(a64 & 0xffffffffu));
+        const unsigned ahi = __builtin_amdgcn_readfirstlane((unsigned)(a64 >> 32));
+        cbase[bb] = ((unsigned long long)ahi << 32) | alo;
+        cstride[bb] = __builtin_amdgcn_readfirstlane((unsigned)(TK * ld * 2));
+        cpitch[bb] = __builtin_amdgcn_readfirstlane((int)(ld * 2));
+    }
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    auto issue_tile = [&](int t) {
+        const int rows = min(N - t * TK, TK);
+        const unsigned st = lds0 + (unsigned)((t % PP_NSTAGE) * C::STAGE);
+#pragma unroll
+        for (int bb = 0; bb < C::CPW; ++bb) {
+            const i32x4 r = make_rsrc((const void*)(cbase[bb] + (unsigned long long)t * cstride[bb]),
+                                      rows * cpitch[bb]);
+            copy16_to_lds(r, st + (wave + PS_WAVES * bb) * 1024, coff[bb]);
+        }
+    };
+    auto stage_of = [&](int j) -> const unsigned char* {
+        return smem + ((j >> 1) % PP_NSTAGE) * C::STAGE;
+    };
+
+    auto m_phase = [&](int j) {
+        if (j > jmax) return;
+        const int jv = j > 0 ? j - 1 : 0;
+        const unsigned char* vs = stage_of(jv) + (jv & 1) * BN * C::VROWB;
+        const unsigned char* ks = stage_of(j) + (j & 1) * BN * C::KROWB;
+        constexpr int NU = C::VBLK + C::KSTEPS;
+        bf16x8 vf[C::VBLK][2];
+        bf16x8 kf[C::KSTEPS];
+        auto load_unit = [&](int u) {
+            if (u < C::VBLK) {
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const unsigned char* vp = vs + (u ? (vx ^ fresh(64 * u)) : vx) + t2 * 16 * C::VROWB;
+                    const bf16x4 lo = lds_read_tr(vp);
+                    const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
+                    vf[u < C::VBLK ? u : 0][t2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            } else {
+                const int st = u - C::VBLK;
+                kf[st] = __builtin_bit_cast(bf16x8, load16(ks + (st ? (kx ^ fresh(32 * st)) : kx)));
+            }
+        };
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        load_unit(0);
+        load_unit(1);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if (u < C::VBLK) {
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2)
+                    acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u][t2], pf[t2], acc[u], 0, 0, 0);
+            } else {
+                const int st = u - C::VBLK;
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s, 0, 0, 0);
+            }
+            if (u + 2 < NU) load_unit(u + 2);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        PipeGroups<0, NU, C::VBLK, 1>::run();
+    };
+
+    auto v_phase = [&](int j) {
+        if (j >= jmax) return;
+        const int kb = fresh(j * BN);
+        if (__builtin_expect((kb + BN > N) || (causal && kb + BN - 1 > wrow0), 0)) {
+            const int lim = causal ? min(N - kb, my_row - kb + 1) : N - kb;
+            const int limh = lim - 8 * half;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (key_of_reg(r) >= limh) s[r] = -INFINITY;
+        }
+        const float a0 = max3(s[0], s[1], s[2]);
+        const float a1 = max3(s[3], s[4], s[5]);
+        const float a2 = max3(s[6], s[7], s[8]);
+        const float a3 = max3(s[9], s[10], s[11]);
+        const float a4 = max3(s[12], s[13], s[14]);
+        const float mx = max3(max3(a0, a1, a2), a3, max3(a4, s[15], s[15]));
+        const f32x2 hm = halves(mx);
+        const float mnew = max3(mref, hm[0], hm[1]);
+        const bool grow = mnew > mref + tau_raw;
+        if (__any(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f((mref - mnew) * c) : 1.f;
+            mref = grow ? mnew : mref;
+            lsum *= alpha;
+#pragma unroll
+            for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[nb][r] *= alpha;
+        }
+        const float mc = (mref == -INFINITY) ? 0.f : mref * c;
+        float ls = lsum;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(s[t2 * 8 + e], c, -mc)),
+                                  __builtin_amdgcn_exp2f(fmaf(s[t2 * 8 + e + 1], c, -mc))};
+                const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
+                ls = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, ls, false);
+                pf[t2][e] = pb[0];
+                pf[t2][e + 1] = pb[1];
+            }
+        }
+        lsum = ls;
+    };
+
+    issue_tile(0);
+    if (ntile > 1) {
+        issue_tile(1);
+        wait_copies<C::CPW>();
+    } else {
+        wait_copies<0>();
+    }
+    phase_barrier();
+    if (grp) phase_barrier();
+    for (int j = 0; j <= nsub; ++j) {
+        __builtin_amdgcn_s_setprio(1);
+        m_phase(j);
+        if (j & 1) {
+            // Copy tile (j+3)/2, then wait for tile (j+1)/2 with only the
+            // copies just issued still in flight.
+            const int ti = (j + 3) >> 1, tw = (j + 1) >> 1;
+            if (ti < ntile) issue_tile(ti);
+            if (tw + 1 < ntile) wait_copies<C::CPW>();
+            else wait_copies<0>();
+        }
+        phase_barrier();
+        __builtin_amdgcn_s_setprio(0);
+        v_phase(j);
+        phase_barrier();
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (!grp) phase_barrier();
+
+    // Epilogue: map-2 waves hand lambda-scaled accumulators to map-1 waves.
+    const f32x2 hl = halves(lsum);
+    const float l = hl[0] + hl[1];
+    phase_barrier();   // every wave is done with the stages (no copy in flight)
+    float* xb = reinterpret_cast<float*>(smem) + rb * (QROWS * DV);
+    if (map == 1) {
+        const float w2 = lambda[h] / l;
+#pragma unroll
+        for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = acc[nb][g * 4 + e] * w2;
+                *reinterpret_cast<f32x4*>(xb + ((nb * 4 + g) * WAVE + lane) * 4) = y;
+            }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (map == 1 || my_row >= N) return;
+    const float w1 = 1.f / l;
+    float ss = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 o2 = *reinterpret_cast<const f32x4*>(xb + ((nb * 4 + g) * WAVE + lane) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float y = acc[nb][g * 4 + e] * w1 - o2[e];
+                acc[nb][g * 4 + e] = y;
+                ss = fmaf(y, y, ss);
+            }
+        }
+    float scale = 1.f;
+    if (rmsnorm) {
+        const f32x2 hs2 = halves(ss);
+        scale = norm_scale / sqrtf((hs2[0] + hs2[1]) / (float)DV + eps);
+    }
+    float* orow = out + (tok0 + my_row) * DV;
+    auto store = [&](auto weight) {
+#pragma unroll
+        for (int nb = 0; nb < C::VBLK; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int ch = nb * 32 + g * 8 + half * 4;
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = acc[nb][g * 4 + e] * scale * weight(ch + e);
+                *reinterpret_cast<f32x4*>(orow + ch) = y;
+            }
+    };
+    if (rmsnorm && norm_weight) store([&](int ch) { return norm_weight[ch]; });
+    else store([](int) { return 1.f; });
 }
 
-hipError_t launch_prefill_pp(const PrefillArgs& a, hipStream_t stream) {
+template <int D, int DV>
+hipError_t launch_ps(const PrefillArgs& a, hipStream_t stream) {
+    using C = PSCfg<D, DV>;
+    const int row_tiles = (a.N + PS_BM - 1) / PS_BM;
+    const int BH = a.B * a.H;
+    const int64_t blocks = (int64_t)BH * row_tiles;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_ps_kernel<D, DV>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((prefill_ps_kernel<D, DV>), dim3((unsigned)blocks), dim3(PS_THREADS),
+                       (size_t)C::LDS, stream, (const __bf16*)a.q1, (const __bf16*)a.q2,
+                       (const __bf16*)a.k1, (const __bf16*)a.k2, (const __bf16*)a.v, a.ldq, a.ldk,
+                       a.ldv, BH, a.H, a.N, a.causal, a.lambda, a.rmsnorm, a.eps, a.norm_scale,
+                       a.norm_weight, a.out, row_tiles, a.hs);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_bf16_supported(int d, int dv) {
+    return (d == 64 && dv == 128) || (d == 64 && dv == 64) || (d == 32 && dv == 64) ||
+           (d == 128 && dv == 128);
+}
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     if (a.d == 64 && a.dv == 128) return launch_pp<64, 128, 2>(a, stream);
     if (a.d == 64 && a.dv == 64) return launch_pp<64, 64, 2>(a, stream);
     if (a.d == 32 && a.dv == 64) return launch_pp<32, 64, 2>(a, stream);
+    if (a.d == 128 && a.dv == 128) return launch_ps<128, 128>(a, stream);
     return hipErrorInvalidValue;
 }
 
