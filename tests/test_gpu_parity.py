@@ -90,7 +90,8 @@ def test_prefill_fp32_shapes(d, dv, N, causal, rms):
     (64, 128, 1, True, False), (64, 128, 31, True, True), (64, 128, 32, True, False),
     (64, 128, 33, True, False), (64, 128, 300, True, True), (64, 128, 517, False, False),
     (64, 128, 257, False, True), (64, 64, 200, True, True), (32, 64, 160, True, False),
-    (128, 128, 190, True, False), (128, 128, 64, False, True),
+    (128, 128, 190, True, False), (128, 128, 64, False, True), (128, 128, 1, True, True),
+    (128, 128, 33, True, False), (128, 128, 128, True, True), (128, 128, 257, False, True),
 ])
 def test_prefill_bf16_shapes(d, dv, N, causal, rms):
     case = W.PrefillCase("bf16_d%d_dv%d_n%d" % (d, dv, N), "bf16", B=2, H=3, N=N, d=d, dv=dv,
