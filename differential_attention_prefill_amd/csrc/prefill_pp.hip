@@ -637,6 +637,8 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     unsigned cstride[C::CPW];
     int cpitch[C::CPW];
 #pragma unroll
+    // Copy blocks as in the d <= 64 kernel: block id of a tile moves 1 KB
+    // (K1 rows, then K2 rows, then V rows), and wave w copies ids w, w+8, ...
     for (int bb = 0; bb < C::CPW; ++bb) {
         const int id = wave + PS_WAVES * bb;
         if (id < 2 * C::KBLK) {
@@ -670,6 +672,10 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         return smem + ((j >> 1) % PP_NSTAGE) * C::STAGE;
     };
 
+    // M(j), j <= jmax: this map's P.V of sub-tile j-1 (4 V^T blocks) and its
+    // scores of sub-tile j (8 key k-steps), one pipeline with the loads two
+    // units ahead; at j = 0 the probabilities are zero, at j = jmax the scores
+    // are dropped (as in the d <= 64 kernel).
     auto m_phase = [&](int j) {
         if (j > jmax) return;
         const int jv = j > 0 ? j - 1 : 0;
@@ -713,6 +719,8 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         PipeGroups<0, NU, C::VBLK, 1>::run();
     };
 
+    // V(j): this map's online softmax of sub-tile j (mask, row maximum, lazy
+    // rescale, probabilities for M(j+1)).
     auto v_phase = [&](int j) {
         if (j >= jmax) return;
         const int kb = fresh(j * BN);
