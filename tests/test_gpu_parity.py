@@ -258,10 +258,11 @@ def _rand_bf16(shape, seed):
     return torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16)
 
 
-def test_prefill_rows_sum_to_one_minus_lambda():
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_rows_sum_to_one_minus_lambda(d):
     # A value tensor of ones reads off the row sums of A1 - lam A2 = 1 - lam.
-    B, H, N, d, dv = 1, 4, 700, 64, 128
-    say("bf16 row-sum invariant N=%d" % N)
+    B, H, N, dv = 1, 4, 700, 128
+    say("bf16 row-sum invariant N=%d d=%d" % (N, d))
     q, k = _rand_bf16((B, H, N, 2 * d), 1), _rand_bf16((B, H, N, 2 * d), 2)
     v = torch.ones((B, H, N, dv), dtype=torch.bfloat16, device=DEV)
     lam = torch.tensor([0.2, 0.8, -0.5, 1.3], device=DEV)
@@ -270,9 +271,10 @@ def test_prefill_rows_sum_to_one_minus_lambda():
     assert (out - want).abs().max().item() < 1e-2
 
 
-def test_prefill_identical_maps_cancel():
-    B, H, N, d, dv = 2, 2, 333, 64, 128
-    say("bf16 identical maps with lambda=1")
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_identical_maps_cancel(d):
+    B, H, N, dv = 2, 2, 333, 128
+    say("bf16 identical maps with lambda=1, d=%d" % d)
     qh, kh = _rand_bf16((B, H, N, d), 3), _rand_bf16((B, H, N, d), 4)
     v = _rand_bf16((B, H, N, dv), 5)
     lam = torch.ones(H, device=DEV)
@@ -280,12 +282,13 @@ def test_prefill_identical_maps_cancel():
     assert out.abs().max().item() <= 1e-6
 
 
-@pytest.mark.parametrize("B,H,N,causal", [(2, 4, 1000, True), (1, 3, 777, False)])
-def test_prefill_bitwise_deterministic(B, H, N, causal):
+@pytest.mark.parametrize("B,H,N,causal,d", [(2, 4, 1000, True, 64), (1, 3, 777, False, 64),
+                                            (2, 2, 900, True, 128)])
+def test_prefill_bitwise_deterministic(B, H, N, causal, d):
     # Many workgroups, repeated launches: results must be bit-identical, and
     # with identical maps and lambda = 1 every output must vanish.
-    say("bf16 determinism B=%d H=%d N=%d causal=%s" % (B, H, N, causal))
-    d, dv = 64, 128
+    say("bf16 determinism B=%d H=%d N=%d causal=%s d=%d" % (B, H, N, causal, d))
+    dv = 128
     qh, kh, v = _rand_bf16((B, H, N, d), 31), _rand_bf16((B, H, N, d), 32), _rand_bf16((B, H, N, dv), 33)
     q, k = _rand_bf16((B, H, N, 2 * d), 34), _rand_bf16((B, H, N, 2 * d), 35)
     lam = torch.linspace(-0.5, 1.5, H, device=DEV)
@@ -298,9 +301,10 @@ def test_prefill_bitwise_deterministic(B, H, N, causal):
         assert z.abs().max().item() <= 1e-6
 
 
-def test_prefill_causality_and_determinism():
-    B, H, N, d, dv = 1, 2, 400, 64, 128
-    say("bf16 causality / determinism")
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_causality_and_determinism(d):
+    B, H, N, dv = 1, 2, 400, 128
+    say("bf16 causality / determinism d=%d" % d)
     q, k, v = _rand_bf16((B, H, N, 2 * d), 6), _rand_bf16((B, H, N, 2 * d), 7), _rand_bf16((B, H, N, dv), 8)
     lam = torch.tensor([0.3, 0.6], device=DEV)
     a = api.diffattn_prefill_packed(q, k, v, lam)
