@@ -108,17 +108,18 @@ __device__ __forceinline__ int fresh(int c) {
     return c;
 }
 
-// Scheduling groups of the pipelined M phase: load units 0 and 1, then for
-// each unit u its matrix products followed by the loads of unit u+2.  Units
-// 0 .. VB-1 are V^T blocks (4 LDS reads, 2*MAPS products), the rest are key
-// k-steps (MAPS reads, MAPS products).
+// Scheduling groups of the pipelined M phase.  Units 0 .. VB-1 are V^T
+// blocks (4 LDS reads, 2*MAPS products), the rest are key k-steps (MAPS reads,
+// MAPS products).  Units 0 and 1 are already in registers (read at the end of
+// the previous M phase): for each unit u its products, then the loads of
+// unit u+2.
 template <int U, int NU, int VB, int MAPS>
-struct PipeGroups {
+struct PipeGroupsN {
     static __device__ __forceinline__ void run() {
-        __builtin_amdgcn_sched_group_barrier(0x008, U < VB ? 2 * MAPS : MAPS, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, U < VB ? 2 * MAPS : MAPS, 0);
         if constexpr (U + 2 < NU)
-            __builtin_amdgcn_sched_group_barrier(0x100, (U + 2) < VB ? 4 : MAPS, 0);   // LDS read
-        if constexpr (U + 1 < NU) PipeGroups<U + 1, NU, VB, MAPS>::run();
+            __builtin_amdgcn_sched_group_barrier(0x100, (U + 2) < VB ? 4 : MAPS, 0);
+        if constexpr (U + 1 < NU) PipeGroupsN<U + 1, NU, VB, MAPS>::run();
     }
 };
 
@@ -204,6 +205,7 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             for (int r = 0; r < 16; ++r) acc[m][nb][r] = 0.f;
     f32x16 s[MAPS];       // scores of the current sub-tile
     bf16x8 pf[MAPS][2];   // probabilities of the previous sub-tile (B operand)
+    bf16x8 vnext[2][2];   // V^T units 0 and 1 of the next M phase, read ahead
 #pragma unroll
     for (int m = 0; m < MAPS; ++m) {
 #pragma unroll
@@ -287,11 +289,22 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // M(j), for j <= jmax: P.V of sub-tile j-1 (both maps share each V^T
     // fragment) and the scores of sub-tile j for both maps, as one software
     // pipeline over units (the V^T blocks, then the key k-steps) with the
-    // loads two units ahead.  At j = 0 the probabilities are all zero and the
+    // loads two units ahead.  Units 0 and 1 arrive in registers from the end
+    // of M(j-1) (from the prologue for M(0)), so the phase starts on products;
+    // at its end M(j) reads them for M(j+1).  At j = 0 the probabilities are all zero and the
     // values of sub-tile 0 stand in, adding exact zeros; at j = jmax the
     // scores come from whatever the stage holds and are never used.  One code
     // path for every step keeps the accumulators in place.  The derived LDS
     // offsets are rematerialised per use (fresh) rather than kept per lane.
+    auto read_v = [&](const unsigned char* vs, int u, bf16x8 (&dst)[2]) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            const unsigned char* vp = vs + (u ? (vx ^ fresh(64 * u)) : vx) + t2 * 16 * C::VROWB;
+            const bf16x4 lo = lds_read_tr(vp);
+            const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
+            dst[t2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
     auto m_phase = [&](int j) {
         if (j > jmax) return;
         const int jv = j > 0 ? j - 1 : 0;
@@ -302,13 +315,7 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         bf16x8 kf[MAPS][C::KSTEPS];
         auto load_unit = [&](int u) {
             if (u < C::VBLK) {
-#pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2) {
-                    const unsigned char* vp = vs + (u ? (vx ^ fresh(64 * u)) : vx) + t2 * 16 * C::VROWB;
-                    const bf16x4 lo = lds_read_tr(vp);
-                    const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
-                    vf[u < C::VBLK ? u : 0][t2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
+                read_v(vs, u, vf[u < C::VBLK ? u : 0]);
             } else {
                 const int st = u - C::VBLK;
 #pragma unroll
@@ -321,8 +328,11 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         for (int m = 0; m < MAPS; ++m)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
-        load_unit(0);
-        load_unit(1);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            vf[0][t2] = vnext[0][t2];
+            vf[1][t2] = vnext[1][t2];
+        }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             if (u < C::VBLK) {
@@ -339,9 +349,13 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             }
             if (u + 2 < NU) load_unit(u + 2);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        PipeGroups<0, NU, C::VBLK, MAPS>::run();
+        // Units 0 and 1 of M(j+1): the values of sub-tile j, visible now (its
+        // keys were read above) and not overwritten before M(j+1).
+        const unsigned char* vsn = stage_of(j) + (j & 1) * BN * C::VROWB;
+        read_v(vsn, 0, vnext[0]);
+        read_v(vsn, 1, vnext[1]);
+        PipeGroupsN<0, NU, C::VBLK, MAPS>::run();
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
     };
 
     // V(j): both online softmaxes of sub-tile j -> probabilities for M(j+1).
@@ -435,6 +449,8 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         wait_copies<0>();
     }
     phase_barrier();            // tile 0 visible
+    read_v(smem, 0, vnext[0]);  // M(0): values of sub-tile 0 (times zero probabilities)
+    read_v(smem, 1, vnext[1]);
     if (grp) phase_barrier();   // group 1 starts one phase later
     // The wave in its matrix phase takes issue priority over the one in its
     // softmax phase on the same SIMD, so the matrix core is fed first.
@@ -618,6 +634,7 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
     f32x16 s;
     bf16x8 pf[2];
+    bf16x8 vnext[2][2];   // V^T units 0 and 1 of the next M phase, read ahead
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
@@ -676,6 +693,15 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // scores of sub-tile j (8 key k-steps), one pipeline with the loads two
     // units ahead; at j = 0 the probabilities are zero, at j = jmax the scores
     // are dropped (as in the d <= 64 kernel).
+    auto read_v = [&](const unsigned char* vs, int u, bf16x8 (&dst)[2]) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            const unsigned char* vp = vs + (u ? (vx ^ fresh(64 * u)) : vx) + t2 * 16 * C::VROWB;
+            const bf16x4 lo = lds_read_tr(vp);
+            const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
+            dst[t2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
     auto m_phase = [&](int j) {
         if (j > jmax) return;
         const int jv = j > 0 ? j - 1 : 0;
@@ -686,13 +712,7 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         bf16x8 kf[C::KSTEPS];
         auto load_unit = [&](int u) {
             if (u < C::VBLK) {
-#pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2) {
-                    const unsigned char* vp = vs + (u ? (vx ^ fresh(64 * u)) : vx) + t2 * 16 * C::VROWB;
-                    const bf16x4 lo = lds_read_tr(vp);
-                    const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
-                    vf[u < C::VBLK ? u : 0][t2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
+                read_v(vs, u, vf[u < C::VBLK ? u : 0]);
             } else {
                 const int st = u - C::VBLK;
                 kf[st] = __builtin_bit_cast(bf16x8, load16(ks + (st ? (kx ^ fresh(32 * st)) : kx)));
@@ -700,8 +720,11 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         };
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
-        load_unit(0);
-        load_unit(1);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            vf[0][t2] = vnext[0][t2];
+            vf[1][t2] = vnext[1][t2];
+        }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             if (u < C::VBLK) {
@@ -714,9 +737,12 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             }
             if (u + 2 < NU) load_unit(u + 2);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        PipeGroups<0, NU, C::VBLK, 1>::run();
+        // Units 0 and 1 of M(j+1): the values of sub-tile j.
+        const unsigned char* vsn = stage_of(j) + (j & 1) * BN * C::VROWB;
+        read_v(vsn, 0, vnext[0]);
+        read_v(vsn, 1, vnext[1]);
+        PipeGroupsN<0, NU, C::VBLK, 1>::run();
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
     };
 
     // V(j): this map's online softmax of sub-tile j (mask, row maximum, lazy
@@ -773,7 +799,9 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     } else {
         wait_copies<0>();
     }
-    phase_barrier();
+    phase_barrier();            // tile 0 visible
+    read_v(smem, 0, vnext[0]);  // M(0): values of sub-tile 0 (times zero probabilities)
+    read_v(smem, 1, vnext[1]);
     if (grp) phase_barrier();
     for (int j = 0; j <= nsub; ++j) {
         __builtin_amdgcn_s_setprio(1);
