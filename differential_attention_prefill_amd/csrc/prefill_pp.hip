@@ -108,18 +108,33 @@ __device__ __forceinline__ int fresh(int c) {
     return c;
 }
 
-// Scheduling groups of the pipelined M phase.  Units 0 .. VB-1 are V^T
-// blocks (4 LDS reads, 2*MAPS products), the rest are key k-steps (MAPS reads,
-// MAPS products).  Units 0 and 1 are already in registers (read at the end of
-// the previous M phase): for each unit u its products, then the loads of
-// unit u+2.
-template <int U, int NU, int VB, int MAPS>
+// Units of the pipelined M phase: 0 .. VB-1 are V^T blocks (4 LDS reads,
+// 2*MAPS products), VB .. NU-1 are key k-steps (MAPS reads, MAPS products).
+// unit_at(p) is the unit at pipeline position p.  V^T units 0 and 1 come first
+// (they are read at the end of the previous M phase); with IL the key
+// k-steps then alternate with the remaining V^T units, so that every load has
+// at least one V^T unit's products between its issue and its use.
+__host__ __device__ constexpr int unit_at(int p, int VB, int NU, bool IL) {
+    if (!IL || p < 2) return p;
+    int v = 2, k = 0;
+    for (int q = 2; q < NU; ++q) {
+        const bool take_k = (k < NU - VB) && ((q % 2 == 0) || v >= VB);
+        if (q == p) return take_k ? VB + k : v;
+        if (take_k) ++k;
+        else ++v;
+    }
+    return -1;
+}
+
+// Scheduling groups of the pipelined M phase: for each position p the
+// products of its unit, then the loads of the unit at position p+PD.
+template <int P, int NU, int VB, int MAPS, bool IL, int PD>
 struct PipeGroupsN {
     static __device__ __forceinline__ void run() {
-        __builtin_amdgcn_sched_group_barrier(0x008, U < VB ? 2 * MAPS : MAPS, 0);
-        if constexpr (U + 2 < NU)
-            __builtin_amdgcn_sched_group_barrier(0x100, (U + 2) < VB ? 4 : MAPS, 0);
-        if constexpr (U + 1 < NU) PipeGroupsN<U + 1, NU, VB, MAPS>::run();
+        __builtin_amdgcn_sched_group_barrier(0x008, unit_at(P, VB, NU, IL) < VB ? 2 * MAPS : MAPS, 0);
+        if constexpr (P + PD < NU)
+            __builtin_amdgcn_sched_group_barrier(0x100, unit_at(P + PD, VB, NU, IL) < VB ? 4 : MAPS, 0);
+        if constexpr (P + 1 < NU) PipeGroupsN<P + 1, NU, VB, MAPS, IL, PD>::run();
     }
 };
 
@@ -334,7 +349,8 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             vf[1][t2] = vnext[1][t2];
         }
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
+        for (int p = 0; p < NU; ++p) {
+            const int u = unit_at(p, C::VBLK, NU, true);
             if (u < C::VBLK) {
 #pragma unroll
                 for (int t2 = 0; t2 < 2; ++t2)
@@ -347,14 +363,14 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                 for (int m = 0; m < MAPS; ++m)
                     s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m][st], qf[m][st], s[m], 0, 0, 0);
             }
-            if (u + 2 < NU) load_unit(u + 2);
+            if (p + 2 < NU) load_unit(unit_at(p + 2, C::VBLK, NU, true));
         }
         // Units 0 and 1 of M(j+1): the values of sub-tile j, visible now (its
         // keys were read above) and not overwritten before M(j+1).
         const unsigned char* vsn = stage_of(j) + (j & 1) * BN * C::VROWB;
         read_v(vsn, 0, vnext[0]);
         read_v(vsn, 1, vnext[1]);
-        PipeGroupsN<0, NU, C::VBLK, MAPS>::run();
+        PipeGroupsN<0, NU, C::VBLK, MAPS, true, 2>::run();
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
     };
 
@@ -550,6 +566,7 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t stream) {
 constexpr int PS_WAVES = 8;
 constexpr int PS_THREADS = WAVE * PS_WAVES;
 constexpr int PS_BM = QROWS * 4;
+constexpr int PS_PD = 4;   // M-phase read-ahead distance, in pipeline units
 
 template <int D, int DV>
 struct PSCfg {
@@ -634,7 +651,10 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
     f32x16 s;
     bf16x8 pf[2];
-    bf16x8 vnext[2][2];   // V^T units 0 and 1 of the next M phase, read ahead
+    // The M phase's loads run PS_PD units ahead; its first PS_PD units (V^T
+    // blocks) are read at the end of the previous M phase.
+    static_assert(PS_PD >= 1 && PS_PD <= C::VBLK, "read-ahead units must be V^T blocks");
+    bf16x8 vnext[PS_PD][2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
@@ -690,7 +710,7 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     };
 
     // M(j), j <= jmax: this map's P.V of sub-tile j-1 (4 V^T blocks) and its
-    // scores of sub-tile j (8 key k-steps), one pipeline with the loads two
+    // scores of sub-tile j (8 key k-steps), one pipeline with the loads PS_PD
     // units ahead; at j = 0 the probabilities are zero, at j = jmax the scores
     // are dropped (as in the d <= 64 kernel).
     auto read_v = [&](const unsigned char* vs, int u, bf16x8 (&dst)[2]) {
@@ -721,10 +741,9 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-            vf[0][t2] = vnext[0][t2];
-            vf[1][t2] = vnext[1][t2];
-        }
+        for (int u = 0; u < PS_PD; ++u)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) vf[u][t2] = vnext[u][t2];
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             if (u < C::VBLK) {
@@ -735,14 +754,14 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                 const int st = u - C::VBLK;
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s, 0, 0, 0);
             }
-            if (u + 2 < NU) load_unit(u + 2);
+            if (u + PS_PD < NU) load_unit(u + PS_PD);
         }
-        // Units 0 and 1 of M(j+1): the values of sub-tile j.
+        // The first units of M(j+1): the values of sub-tile j.
         const unsigned char* vsn = stage_of(j) + (j & 1) * BN * C::VROWB;
-        read_v(vsn, 0, vnext[0]);
-        read_v(vsn, 1, vnext[1]);
-        PipeGroupsN<0, NU, C::VBLK, 1>::run();
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int u = 0; u < PS_PD; ++u) read_v(vsn, u, vnext[u]);
+        PipeGroupsN<0, NU, C::VBLK, 1, false, PS_PD>::run();
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * PS_PD, 0);
     };
 
     // V(j): this map's online softmax of sub-tile j (mask, row maximum, lazy
@@ -800,8 +819,9 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         wait_copies<0>();
     }
     phase_barrier();            // tile 0 visible
-    read_v(smem, 0, vnext[0]);  // M(0): values of sub-tile 0 (times zero probabilities)
-    read_v(smem, 1, vnext[1]);
+#pragma unroll
+    for (int u = 0; u < PS_PD; ++u)  // M(0): values of sub-tile 0 (times zero probabilities)
+        read_v(smem, u, vnext[u]);
     if (grp) phase_barrier();
     for (int j = 0; j <= nsub; ++j) {
         __builtin_amdgcn_s_setprio(1);
