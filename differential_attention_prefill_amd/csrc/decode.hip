@@ -57,6 +57,15 @@ constexpr float DEC_TAU = 8.0f;
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Cache stream: every byte is read once, so the loads carry the non-temporal
+// hint (no reuse to keep in the caches; measured 6.5-7.4 TB/s for a plain
+// streaming read on this device against 6.1-6.3 TB/s without it).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Row slot rho of score tile t holds key (rho/4)*8 + t*4 + rho%4 of the
 // 32-key tile, so that the accumulator registers of tiles 0 and 1 line up as
 // 8 consecutive keys per lane group: the B operand of the next product.
@@ -142,15 +151,15 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                 const bool ok = key < cend;
                 const __bf16* src = kc + (kv0 + (ok ? key : 0)) * DEC_D + grp * 8;
     #pragma unroll
-                for (int s = 0; s < 4; ++s) kreg[t][s] = ok ? ld16(src + s * 32) : make_uint4(0, 0, 0, 0);
+                for (int s = 0; s < 4; ++s) kreg[t][s] = ok ? ld16_stream(src + s * 32) : make_uint4(0, 0, 0, 0);
             }
     #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int item = lane + 64 * i;
                 const int kp = item >> 4, ch = item & 15;
                 const int key = kb + 2 * kp;
-                vreg[i][0] = key < cend ? ld16(vc + (kv0 + key) * DEC_D + ch * 8) : make_uint4(0, 0, 0, 0);
-                vreg[i][1] = key + 1 < cend ? ld16(vc + (kv0 + key + 1) * DEC_D + ch * 8)
+                vreg[i][0] = key < cend ? ld16_stream(vc + (kv0 + key) * DEC_D + ch * 8) : make_uint4(0, 0, 0, 0);
+                vreg[i][1] = key + 1 < cend ? ld16_stream(vc + (kv0 + key + 1) * DEC_D + ch * 8)
                                             : make_uint4(0, 0, 0, 0);
             }
         };
