@@ -16,8 +16,8 @@
 //    running maxima and normalisers, two fp32 accumulators (the maps rescale
 //    independently, so an exact single pass needs one per map).
 //  - Each 32-key sub-tile j is two phases per wave: M(j) issues the matrix
-//    products (P.V of sub-tile j-1 for both maps, then the scores of
-//    sub-tile j for both maps), V(j) runs both online softmaxes of sub-tile
+//    products (P.V of sub-tile j-1 and the scores of sub-tile j, both maps,
+//    as one pipeline over operand units), V(j) runs both online softmaxes of sub-tile
 //    j on the vector ALU.  The waves form two groups, and the second runs one
 //    phase behind the first, with a workgroup barrier after every phase:
 //    while one group's matrix products occupy a SIMD's matrix core, the
@@ -303,14 +303,16 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
 
     // M(j), for j <= jmax: P.V of sub-tile j-1 (both maps share each V^T
     // fragment) and the scores of sub-tile j for both maps, as one software
-    // pipeline over units (the V^T blocks, then the key k-steps) with the
-    // loads two units ahead.  Units 0 and 1 arrive in registers from the end
-    // of M(j-1) (from the prologue for M(0)), so the phase starts on products;
-    // at its end M(j) reads them for M(j+1).  At j = 0 the probabilities are all zero and the
-    // values of sub-tile 0 stand in, adding exact zeros; at j = jmax the
-    // scores come from whatever the stage holds and are never used.  One code
-    // path for every step keeps the accumulators in place.  The derived LDS
-    // offsets are rematerialised per use (fresh) rather than kept per lane.
+    // pipeline over units in unit_at order (V^T blocks 0 and 1, then the key
+    // k-steps alternating with the other V^T blocks) with the loads two
+    // positions ahead.  V^T units 0 and 1 arrive in registers from the end of
+    // M(j-1) (from the prologue for M(0)), so the phase starts on products;
+    // at its end M(j) reads them for M(j+1).  At j = 0 the probabilities are
+    // all zero and the values of sub-tile 0 stand in, adding exact zeros; at
+    // j = jmax the scores come from whatever the stage holds and are never
+    // used.  One code path for every step keeps the accumulators in place.
+    // The derived LDS offsets are rematerialised per use (fresh) rather than
+    // kept per lane.
     auto read_v = [&](const unsigned char* vs, int u, bf16x8 (&dst)[2]) {
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
