@@ -100,6 +100,41 @@ def test_prefill_bf16_shapes(d, dv, N, causal, rms):
     _prefill_case_check(case)
 
 
+@pytest.mark.parametrize("d,dv,mode,causal", [
+    (64, 128, "wide", True), (64, 128, "growing", True), (64, 128, "growing", False),
+    (128, 128, "wide", False), (128, 128, "growing", True),
+])
+def test_prefill_bf16_rescale_stress(d, dv, mode, causal):
+    """Logits far wider than the unit-variance workloads, so that row maxima
+    keep growing past the lazy-rescale threshold: "wide" scales the queries
+    by 6 (scaled scores with a spread of about 6); "growing" adds to key j of
+    each map (j/N) * A * u_m along a fixed unit direction u_m (A = 30 sqrt(d)
+    for map 1, 20 sqrt(d) for map 2), so a query's scores drift by up to about
+    30 over the sequence, upward for half the queries (a new maximum in most
+    sub-tiles, at different times in the two maps) and downward for the rest
+    (probabilities that underflow)."""
+    N = 700
+    case = W.PrefillCase("bf16_%s_d%d" % (mode, d), "bf16", B=1, H=2, N=N, d=d, dv=dv, layer=3,
+                         rmsnorm=True, seed=4100 + d, causal=causal)
+    say("bf16 prefill rescale stress %s d=%d causal=%s" % (mode, d, causal))
+    inp = W.make_prefill(case, device="cpu")
+    g = torch.Generator().manual_seed(4200 + d)
+    if mode == "wide":
+        inp["q"] = (inp["q"].float() * 6.0).to(torch.bfloat16)
+    else:
+        ramp = (torch.arange(N, dtype=torch.float32) / N).reshape(1, 1, N, 1)
+        k = inp["k"].float()
+        for m, amp in ((0, 30.0), (1, 20.0)):
+            u = torch.randn(d, generator=g)
+            u = u / u.norm()
+            k[..., m * d:(m + 1) * d] += ramp * (amp * math.sqrt(d)) * u
+        inp["k"] = k.to(torch.bfloat16)
+    lam_gpu = gpu_lambda(inp, case.layer)
+    out = run_prefill_gpu(case, inp, lam_gpu).cpu().numpy()
+    ref = run_prefill_oracle(case, inp, lam_gpu.cpu().numpy())
+    compare(out, ref, "bf16", case.name)
+
+
 def test_prefill_bf16_norm_weight():
     case = W.PrefillCase("bf16_weighted_norm", "bf16", B=1, H=2, N=130, d=64, dv=128, layer=6,
                          rmsnorm=True, seed=77)
