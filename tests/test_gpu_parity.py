@@ -412,6 +412,39 @@ def test_decode_ragged_lengths(lens):
     compare(out.cpu().numpy(), ref, "bf16", case.name)
 
 
+@pytest.mark.parametrize("mode", ["wide", "growing"])
+def test_decode_rescale_stress(mode):
+    """Decode over several chunks per sequence with logits far wider than the
+    workload's: "wide" scales the queries by 6; "growing" adds (j/L) * 30
+    sqrt(D) * u to cached key j along a fixed unit direction u, so a head's
+    scores drift by up to about 30 across the sequence (new maxima inside and
+    across chunks, or underflowing probabilities), which exercises the lazy
+    rescale in the split kernel and the log-sum-exp weights of the merge."""
+    lens = [9000, 4097, 2500, 1]
+    case = W.DecodeCase("decode_stress_%s" % mode, B=len(lens), Hq=8, Hkv=2, D=128,
+                        Lmin=1, Lmax=max(lens), layer=5, seed=4300 + len(mode))
+    say("decode rescale stress %s lens=%s" % (mode, lens))
+    inp = W.make_decode(case, device="cpu")
+    inp["seq_lens"] = torch.tensor(lens, dtype=torch.int32)
+    if mode == "wide":
+        inp["q"] = (inp["q"].float() * 6.0).to(torch.bfloat16)
+    else:
+        g = torch.Generator().manual_seed(4400)
+        u = torch.randn(case.D, generator=g)
+        u = u / u.norm()
+        k = inp["k_cache"].float()
+        for b, L in enumerate(lens):
+            ramp = (torch.arange(L, dtype=torch.float32) / L).reshape(1, L, 1)
+            k[b, :, :L] += ramp * (30.0 * math.sqrt(case.D)) * u
+        inp["k_cache"] = k.to(torch.bfloat16)
+    dev = {x: inp[x].to(DEV) for x in ("q", "k_cache", "v_cache", "seq_lens")}
+    lam_gpu = gpu_lambda(inp, case.layer)
+    out = api.diffattn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["seq_lens"], lam_gpu)
+    ref = oracle.decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"],
+                        lam_gpu.cpu().numpy())
+    compare(out.cpu().numpy(), ref, "bf16", case.name)
+
+
 @pytest.mark.parametrize("hq,hkv", [(4, 2), (16, 2), (32, 8), (8, 4)])
 def test_decode_group_sizes(hq, hkv):
     case = W.DecodeCase("decode_g%d" % (hq // hkv), B=2, Hq=hq, Hkv=hkv, D=128, Lmin=500,
