@@ -33,6 +33,8 @@
 // column 0 holding q1 in the first d channels and zeros in the rest, column 1
 // zeros then q2, so the D-wide dot products are q1.k1 and q2.k2 and V is read
 // once for both maps.  Scores are scaled by 1/sqrt(d).
+#include <atomic>
+
 #include "kernels.h"
 
 namespace diffattn {
@@ -373,17 +375,18 @@ size_t decode_workspace_floats(int B, int Hq, int D, int max_len) {
 // Workgroups of the persistent split kernel: two per CU (its register use
 // allows two per CU), never more than there can be items.
 static int decode_split_grid(int B, int Hkv, int S) {
-    static int cus[64] = {0};
+    // CU count per device, cached (a repeated first query is harmless).
+    static std::atomic<int> cus[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    int n = dev >= 0 && dev < 64 ? cus[dev].load(std::memory_order_relaxed) : 0;
+    if (n == 0) {
+        if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
             n = 256;
-        cus[dev] = n;
+        if (dev >= 0 && dev < 64) cus[dev].store(n, std::memory_order_relaxed);
     }
     const int64_t items = (int64_t)B * Hkv * S;
-    const int64_t want = 2 * (int64_t)cus[dev];
+    const int64_t want = 2 * (int64_t)n;
     return (int)(items < want ? items : want);
 }
 

@@ -49,6 +49,8 @@
 //    takes part in every barrier); only those that straddle the diagonal or
 //    the sequence end are masked.  Heavy query tiles are scheduled first, and
 //    consecutive workgroups take different heads.
+#include <atomic>
+
 #include "kernels.h"
 #include "bf16_tile.h"
 
@@ -537,6 +539,22 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     else store([](int) { return 1.f; });
 }
 
+// Raises a kernel's dynamic-LDS limit on the current device.  The attribute
+// belongs to the device, so it is set once on each device; `done` only caches
+// that (setting it again is harmless, so concurrent first calls are safe).
+constexpr int MAX_DEVICES = 64;
+template <typename K>
+hipError_t ensure_lds_limit(K kernel, int bytes, std::atomic<bool>* done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < MAX_DEVICES;
+    if (cached && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+    e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && cached) done[dev].store(true, std::memory_order_release);
+    return e;
+}
+
 template <int D, int DV, int MAPS>
 hipError_t launch_pp(const PrefillArgs& a, hipStream_t stream) {
     using C = PPCfg<D, DV, MAPS>;
@@ -544,13 +562,9 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const int64_t blocks = (int64_t)BH * row_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    static bool attr_set = false;    // raise the dynamic-LDS limit once per process
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_pp_kernel<D, DV, MAPS>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<bool> lds_ok[MAX_DEVICES];
+    const hipError_t e = ensure_lds_limit(prefill_pp_kernel<D, DV, MAPS>, C::LDS, lds_ok);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_pp_kernel<D, DV, MAPS>), dim3((unsigned)blocks), dim3(PP_THREADS),
                        (size_t)C::LDS, stream, (const __bf16*)a.q1, (const __bf16*)a.q2,
                        (const __bf16*)a.k1, (const __bf16*)a.k2, (const __bf16*)a.v, a.ldq, a.ldk,
@@ -908,13 +922,9 @@ hipError_t launch_ps(const PrefillArgs& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const int64_t blocks = (int64_t)BH * row_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_ps_kernel<D, DV>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<bool> lds_ok[MAX_DEVICES];
+    const hipError_t e = ensure_lds_limit(prefill_ps_kernel<D, DV>, C::LDS, lds_ok);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_ps_kernel<D, DV>), dim3((unsigned)blocks), dim3(PS_THREADS),
                        (size_t)C::LDS, stream, (const __bf16*)a.q1, (const __bf16*)a.q2,
                        (const __bf16*)a.k1, (const __bf16*)a.k2, (const __bf16*)a.v, a.ldq, a.ldk,
