@@ -87,8 +87,8 @@ def main():
                          "a plain copy of known size that calibrates HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU; sharding across GPUs is a design only, with no "
+              "launch path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
