@@ -260,6 +260,42 @@ def measure_extras(dev, reps):
     from differential_attention_prefill_amd import workloads as W
 
     extras = {}
+    # The other prefill workloads the operator is specified on, each timed on
+    # its own: the tiny fp32 case (vector-ALU path, launch-bound: no roofline
+    # claim), the V1 norm workload at N = 2048 and the 32k needle workload
+    # (bf16 matrix-core roofline), the latter with the last query's SNR
+    # towards its needle read off the kernel (probe values).
+    from differential_attention_prefill_amd import snr
+    per_cfg = {}
+    for c in (W.TINY_FP32, W.V1_NORM, W.NEEDLE_32K):
+        print("# extras: %s" % c.name, file=sys.stderr, flush=True)
+        inp = W.make_prefill(c, device=dev)
+        lam = api.diffattn_lambda(*(inp[x].contiguous() for x in ("lq1", "lk1", "lq2", "lk2")),
+                                  layer=c.layer)
+        scale = (1.0 - api.diffattn_lambda_init(c.layer)) if c.rmsnorm else 1.0
+        out = torch.empty((c.B, c.H, c.N, c.dv), dtype=torch.float32, device=dev)
+        ms = _time_launches(lambda: api.diffattn_prefill_packed(
+            inp["q"], inp["k"], inp["v"], lam, causal=c.causal, rmsnorm=c.rmsnorm, eps=c.eps,
+            norm_scale=scale, out=out), max(reps, 20))
+        f = prefill_flops(c)
+        rec = {"dtype": c.dtype, "avg_launch_ms": round(ms, 4), "algorithmic_flops_per_launch": f,
+               "achieved_tflops": round(f / (ms * 1e-3) / 1e12, 2)}
+        if c.dtype == "bf16":
+            rec["frac_of_bf16_peak"] = round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if c.n_needles:
+            # At d = 64 the 5x needle scores about 40 above the noise, so the
+            # noise weight of the last query sits far below fp32 resolution:
+            # the kernel reads the signal's share of the row weight; the SNRs
+            # themselves come from the fp64 oracle.
+            r = snr.noise_sweep_point(inp["q"], inp["k"], lam, inp["needles"][:, 0],
+                                      causal=c.causal)
+            rec["last_query_signal_share_mean"] = {"plain": round(float(r["plain_signal"].mean()), 6),
+                                                   "diff": round(float(r["diff_signal"].mean()), 6)}
+        per_cfg[c.name] = rec
+        del inp, out
+        torch.cuda.empty_cache()
+    extras["prefill_workloads"] = per_cfg
+
     # V2 prefill: doubled query heads over shared K/V heads, D = 128 for both maps.
     c = W.V2_PREFILL_32K
     print("# extras: %s" % c.name, file=sys.stderr, flush=True)
