@@ -584,15 +584,19 @@ constexpr int PS_THREADS = WAVE * PS_WAVES;
 constexpr int PS_BM = QROWS * 4;
 constexpr int PS_PD = 4;   // M-phase read-ahead distance, in pipeline units
 
-template <int D, int DV>
+// SK: both maps read one key tensor (the V2 layout, where the two query heads
+// of a pair share their K/V head): the stage holds it once and both waves of
+// a row block read the same key rows.
+template <int D, int DV, bool SK>
 struct PSCfg {
     static constexpr int KC = D / 8;
     static constexpr int VC = DV / 8;
     static constexpr int KROWB = D * 2;
     static constexpr int VROWB = DV * 2;
-    static constexpr int K2_OFF = TK * KROWB;
-    static constexpr int V_OFF = 2 * TK * KROWB;
-    static constexpr int STAGE = 2 * TK * KROWB + TK * VROWB;
+    static constexpr int NK = SK ? 1 : 2;             // key regions per stage
+    static constexpr int K2_OFF = SK ? 0 : TK * KROWB;
+    static constexpr int V_OFF = NK * TK * KROWB;
+    static constexpr int STAGE = NK * TK * KROWB + TK * VROWB;
     static constexpr int KBLK = TK * KROWB / 1024;
     static constexpr int NCOPY = STAGE / 1024;
     static constexpr int CPW = NCOPY / PS_WAVES;
@@ -606,7 +610,7 @@ struct PSCfg {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int D, int DV>
+template <int D, int DV, bool SK>
 __global__ void __launch_bounds__(PS_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                    const __bf16* __restrict__ k1, const __bf16* __restrict__ k2,
@@ -615,7 +619,7 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                    int rmsnorm, float eps, float norm_scale,
                    const float* __restrict__ norm_weight, float* __restrict__ out,
                    int row_tiles, HeadStrides hs) {
-    using C = PSCfg<D, DV>;
+    using C = PSCfg<D, DV, SK>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int tid = threadIdx.x;
@@ -694,16 +698,16 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // (K1 rows, then K2 rows, then V rows), and wave w copies ids w, w+8, ...
     for (int bb = 0; bb < C::CPW; ++bb) {
         const int id = wave + PS_WAVES * bb;
-        if (id < 2 * C::KBLK) {
+        if (id < C::NK * C::KBLK) {
             const int row = (id % C::KBLK) * C::KRPI + lane / C::KC;
             coff[bb] = row * (int)ldk * 2 + (((lane % C::KC) ^ k_swz<D>(row)) * 16);
         } else {
-            const int row = (id - 2 * C::KBLK) * C::VRPI + lane / C::VC;
+            const int row = (id - C::NK * C::KBLK) * C::VRPI + lane / C::VC;
             coff[bb] = row * (int)ldv * 2 + (((lane % C::VC) ^ v_swz<DV>(row)) * 16);
         }
-        const __bf16* src = id < C::KBLK ? k1 : (id < 2 * C::KBLK ? k2 : v);
-        const int64_t ld = id < 2 * C::KBLK ? ldk : ldv;
-        const unsigned long long a64 = (unsigned long long)(src + (id < 2 * C::KBLK ? koff : voff));
+        const __bf16* src = id < C::KBLK ? k1 : (id < C::NK * C::KBLK ? k2 : v);
+        const int64_t ld = id < C::NK * C::KBLK ? ldk : ldv;
+        const unsigned long long a64 = (unsigned long long)(src + (id < C::NK * C::KBLK ? koff : voff));
         const unsigned alo = __builtin_amdgcn_readfirstlane((unsigned)(a64 & 0xffffffffu));
         const unsigned ahi = __builtin_amdgcn_readfirstlane((unsigned)(a64 >> 32));
         cbase[bb] = ((unsigned long long)ahi << 32) | alo;
@@ -915,17 +919,17 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     else store([](int) { return 1.f; });
 }
 
-template <int D, int DV>
+template <int D, int DV, bool SK>
 hipError_t launch_ps(const PrefillArgs& a, hipStream_t stream) {
-    using C = PSCfg<D, DV>;
+    using C = PSCfg<D, DV, SK>;
     const int row_tiles = (a.N + PS_BM - 1) / PS_BM;
     const int BH = a.B * a.H;
     const int64_t blocks = (int64_t)BH * row_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     static std::atomic<bool> lds_ok[MAX_DEVICES];
-    const hipError_t e = ensure_lds_limit(prefill_ps_kernel<D, DV>, C::LDS, lds_ok);
+    const hipError_t e = ensure_lds_limit(prefill_ps_kernel<D, DV, SK>, C::LDS, lds_ok);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_ps_kernel<D, DV>), dim3((unsigned)blocks), dim3(PS_THREADS),
+    hipLaunchKernelGGL((prefill_ps_kernel<D, DV, SK>), dim3((unsigned)blocks), dim3(PS_THREADS),
                        (size_t)C::LDS, stream, (const __bf16*)a.q1, (const __bf16*)a.q2,
                        (const __bf16*)a.k1, (const __bf16*)a.k2, (const __bf16*)a.v, a.ldq, a.ldk,
                        a.ldv, BH, a.H, a.N, a.causal, a.lambda, a.rmsnorm, a.eps, a.norm_scale,
@@ -944,7 +948,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     if (a.d == 64 && a.dv == 128) return launch_pp<64, 128, 2>(a, stream);
     if (a.d == 64 && a.dv == 64) return launch_pp<64, 64, 2>(a, stream);
     if (a.d == 32 && a.dv == 64) return launch_pp<32, 64, 2>(a, stream);
-    if (a.d == 128 && a.dv == 128) return launch_ps<128, 128>(a, stream);
+    if (a.d == 128 && a.dv == 128)
+        return a.k1 == a.k2 ? launch_ps<128, 128, true>(a, stream) : launch_ps<128, 128, false>(a, stream);
     return hipErrorInvalidValue;
 }
 
