@@ -49,7 +49,7 @@ constexpr int DEC_D = 128;             // head width
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
 constexpr int DEC_TILE = 32;           // keys per wave iteration
-constexpr int DEC_CHUNK = 2048;        // keys per work item (one split)
+constexpr int DEC_CHUNK = 4096;        // keys per work item (one split)
 constexpr int DEC_ITERS = DEC_CHUNK / (DEC_TILE * DEC_WAVES);
 constexpr int DEC_GROUP_MAX = 16;      // query heads per KV head that fit the MFMA columns
 constexpr int DEC_VROW = DEC_TILE * 2 + 16;     // bytes per channel row of V^T (+pad)

@@ -395,7 +395,7 @@ def _decode_check(case, fill_unused=None):
 
 
 @pytest.mark.parametrize("lens", [[1, 2, 31, 33], [1023, 1024, 1025, 3000], [4096, 777, 4095, 64],
-                                  [2047, 2048, 2049, 4097]])
+                                  [2047, 2048, 2049, 4097], [8191, 8192, 8193, 12289]])
 def test_decode_ragged_lengths(lens):
     case = W.DecodeCase("decode_small_%d" % lens[0], B=len(lens), Hq=8, Hkv=2, D=128,
                         Lmin=1, Lmax=max(lens), layer=2, seed=sum(lens))
@@ -470,7 +470,7 @@ def test_decode_invalid_device_length_gives_zeros():
 def test_decode_many_items_with_invalid_lengths():
     # More (sequence, KV head, chunk) items than workgroups, so every
     # workgroup strides over several, with out-of-range lengths in between.
-    B, max_len = 64, 6144
+    B, max_len = 64, 12288
     case = W.DecodeCase("decode_items", B=B, Hq=16, Hkv=8, D=128, Lmin=1, Lmax=max_len, layer=3,
                         seed=77)
     say("decode %d sequences, several chunks each, invalid lengths interleaved" % B)
