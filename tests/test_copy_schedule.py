@@ -57,7 +57,10 @@ def simulate(kv_end, cpw, tk=64, bn=32):
     return ntile, last_read, first_read, issue_phase, done_phase
 
 
-@pytest.mark.parametrize("cpw", [2, 3, 4])
+# Copies per wave and tile in the kernels built: 2 (d = 32, dv = 64), 3
+# (d = 64, dv = 64; single map d = 64, dv = 128), 4 (d = 64, dv = 128; d = 128
+# with one shared key tensor) and 6 (d = 128 with two key tensors).
+@pytest.mark.parametrize("cpw", [2, 3, 4, 6])
 def test_copy_schedule_invariants(cpw):
     extents = list(range(1, 64 * 40 + 1)) + [4095, 4096, 4097, 32768, 65536]
     for kv_end in extents:
