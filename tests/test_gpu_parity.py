@@ -365,6 +365,24 @@ def test_prefill_separate_tensors_match_packed():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_one_key_tensor_for_both_maps(d):
+    # K1 and K2 the same tensor (one pointer): at d = 128 this selects the
+    # stage layout that holds the keys once; against the oracle and against
+    # the same keys passed as two distinct tensors (bitwise).
+    B, H, N, dv = 2, 3, 300, 128
+    say("bf16 prefill, K1 = K2 (one tensor), d=%d N=%d" % (d, N))
+    q1, q2 = _rand_bf16((B, H, N, d), 21), _rand_bf16((B, H, N, d), 22)
+    k, v = _rand_bf16((B, H, N, d), 23), _rand_bf16((B, H, N, dv), 24)
+    lam = torch.tensor([0.4, -0.2, 0.9], device=DEV)
+    shared = api.diffattn_prefill(q1, q2, k, k, v, lam)
+    separate = api.diffattn_prefill(q1, q2, k, k.clone(), v, lam)
+    torch.cuda.synchronize()
+    assert torch.equal(shared, separate)
+    ref = oracle.prefill(q1.cpu(), q2.cpu(), k.cpu(), k.cpu(), v.cpu(), lam.cpu().numpy(), causal=True)
+    compare(shared.cpu().numpy(), ref, "bf16", "one key tensor d=%d" % d)
+
+
 def test_prefill_rejects_host_pointer():
     lib = api.load_library()
     host = torch.zeros((1, 1, 16, 128), dtype=torch.bfloat16)
