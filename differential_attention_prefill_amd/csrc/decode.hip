@@ -17,8 +17,10 @@
 //    query heads of the group (both heads of every pair).  Each of its 4 waves takes every
 //    4th 32-key tile of the chunk.  Scores come from v_mfma_f32_16x16x32_bf16
 //    as S^T = K . Q^T (keys x query heads, the 16 columns padded with zero
-//    heads); probabilities go from registers into O^T += V^T . P^T with V^T
-//    staged through a per-wave LDS tile written transposed.  Each head keeps
+//    heads); probabilities go from registers into O^T += V^T . P^T.  Each V
+//    tile is copied from global memory straight into one of the wave's two
+//    LDS tiles (buffer loads that write LDS, one tile ahead) and its V^T
+//    fragments are read with the transpose load.  Each head keeps
 //    its own running maximum / normaliser / accumulator; the waves' states are
 //    merged in LDS and one partial state (O, m, l) per head and split is
 //    written to the workspace.
@@ -52,8 +54,8 @@ constexpr int DEC_TILE = 32;           // keys per wave iteration
 constexpr int DEC_CHUNK = 4096;        // keys per work item (one split)
 constexpr int DEC_ITERS = DEC_CHUNK / (DEC_TILE * DEC_WAVES);
 constexpr int DEC_GROUP_MAX = 16;      // query heads per KV head that fit the MFMA columns
-constexpr int DEC_VROW = DEC_TILE * 2 + 16;     // bytes per channel row of V^T (+pad)
-constexpr int DEC_VBYTES = DEC_D * DEC_VROW;    // one wave's V^T tile
+constexpr int DEC_VROWB = DEC_D * 2;            // bytes per cached V row
+constexpr int DEC_VBYTES = DEC_TILE * DEC_VROWB; // one V tile, token-major (8 KB)
 constexpr int DEC_STATE = DEC_D + 2;            // floats per partial state: O[D], m*c, l
 constexpr float DEC_TAU = 8.0f;
 
@@ -68,6 +70,44 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// V tiles reach LDS straight from global memory (buffer loads that write LDS:
+// no staging registers) and leave it through the gfx950 transpose load, which
+// hands each lane 4 consecutive keys of one channel.  Rows are stored with
+// their 32-byte channel slots XOR-swizzled by the row's low 3 bits, so the 4
+// rows one 16-lane group reads land in distinct banks.
+__device__ __forceinline__ int vslot_swz(int row) { return row & 7; }
+
+// Raw buffer descriptor (gfx9-family layout): base, stride 0, byte extent;
+// loads at offsets >= `bytes` return zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+    const unsigned long long a = (unsigned long long)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(size_t)((__attribute__((address_space(3))) const unsigned char*)p);
+}
+// 16 bytes per lane from global memory into LDS at lds_base + 16*lane, with the
+// non-temporal hint.  The compiler does not track these loads; the kernel waits
+// for them through the waits it emits for later loads (loads complete in order).
+__device__ __forceinline__ void copy16_to_lds_nt(i32x4 rsrc, unsigned lds_base, int voff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
+}
+__device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<unsigned char*>(p)));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
 // Row slot rho of score tile t holds key (rho/4)*8 + t*4 + rho%4 of the
 // 32-key tile, so that the accumulator registers of tiles 0 and 1 line up as
 // 8 consecutive keys per lane group: the B operand of the next product.
@@ -78,12 +118,12 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens, int B,
                     int Hq, int Hkv, int max_len, int max_splits, float* __restrict__ ws,
                     int qhalf, float c) {
-    // Per-wave V^T tiles during the stream; reused as the wave-merge buffer.
-    __shared__ __attribute__((aligned(16))) unsigned char lds[DEC_WAVES * DEC_VBYTES];
+    // Two V tiles per wave during the stream; reused as the wave-merge buffer.
+    __shared__ __attribute__((aligned(16))) unsigned char lds[DEC_WAVES * 2 * DEC_VBYTES];
     __shared__ float merge_m[DEC_WAVES][DEC_GROUP_MAX];
     __shared__ float merge_l[DEC_WAVES][DEC_GROUP_MAX];
-    static_assert(DEC_WAVES * DEC_GROUP_MAX * DEC_D * 4 <= DEC_WAVES * DEC_VBYTES,
-                  "merge buffer must fit in the V^T tiles");
+    static_assert(DEC_WAVES * DEC_GROUP_MAX * DEC_D * 4 <= DEC_WAVES * 2 * DEC_VBYTES,
+                  "merge buffer must fit in the V tiles");
     float (*merge_o)[DEC_GROUP_MAX][DEC_D] = reinterpret_cast<float (*)[DEC_GROUP_MAX][DEC_D]>(lds);
 
     const int tid = threadIdx.x;
@@ -141,11 +181,10 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
     #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // Prefetch registers: K fragments in A-operand order, V rows for the
-        // transposed LDS store (lane = 4 items of (key pair, 8-channel chunk)).
+        // Prefetch registers: K fragments in A-operand order.  V tiles go to
+        // this wave's two LDS tiles (tile it in tile it % 2).
         uint4 kreg[2][4];
-        uint4 vreg[4][2];
-        auto fetch = [&](int it) {
+        auto fetch_k = [&](int it) {
             const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
     #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -155,39 +194,45 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
     #pragma unroll
                 for (int s = 0; s < 4; ++s) kreg[t][s] = ok ? ld16_stream(src + s * 32) : make_uint4(0, 0, 0, 0);
             }
+        };
+        const unsigned vlds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds + wave * 2 * DEC_VBYTES));
+        auto fetch_v = [&](int it) {
+            const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
+            // Rows past the chunk end read as zeros (their probabilities are 0).
+            const int rows = max(0, min(DEC_TILE, cend - kb));
+            const i32x4 r = make_rsrc(vc + (kv0 + kb) * DEC_D, rows * DEC_VROWB);
+            const unsigned dst = vlds0 + (unsigned)((it & 1) * DEC_VBYTES);
     #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int item = lane + 64 * i;
-                const int kp = item >> 4, ch = item & 15;
-                const int key = kb + 2 * kp;
-                vreg[i][0] = key < cend ? ld16_stream(vc + (kv0 + key) * DEC_D + ch * 8) : make_uint4(0, 0, 0, 0);
-                vreg[i][1] = key + 1 < cend ? ld16_stream(vc + (kv0 + key + 1) * DEC_D + ch * 8)
-                                            : make_uint4(0, 0, 0, 0);
+            for (int bb = 0; bb < DEC_VBYTES / 1024; ++bb) {
+                // Lane l of block bb fills physical row 4*bb + l/16, 16-byte
+                // chunk l%16, which holds logical chunk (l%16) ^ 2*swz(row).
+                const int row = 4 * bb + (lane >> 4);
+                const int lc = (lane & 15) ^ (2 * vslot_swz(row));
+                copy16_to_lds_nt(r, dst + bb * 1024, row * DEC_VROWB + lc * 16);
             }
         };
+        // V^T fragment of 16 channels (block blk) from the tile at vt: lane
+        // (i = lane % 16, G = lane / 16) gets keys 8G .. 8G+7 of channel
+        // 16*blk + i; within a 16-lane group lane j points at row 8G + j/4 (+4),
+        // channels 16*blk + 4*(j%4) .. +3.
+        const int vr0 = 8 * grp + (col >> 2);
+        const int vcb = 8 * (col & 3);                 // byte offset of the 4 channels in the slot
+        auto vfrag = [&](const unsigned char* vt, int blk) -> bf16x8 {
+            const unsigned char* p0 = vt + vr0 * DEC_VROWB + ((blk ^ vslot_swz(vr0)) * 32) + vcb;
+            const unsigned char* p1 = vt + (vr0 + 4) * DEC_VROWB + ((blk ^ vslot_swz(vr0 + 4)) * 32) + vcb;
+            const bf16x4 lo = lds_read_tr(p0);
+            const bf16x4 hi = lds_read_tr(p1);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
 
-        fetch(0);
+        fetch_v(0);
+        fetch_k(0);
         for (int it = 0; it < DEC_ITERS; ++it) {
             const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
             const bool active = kb < cend;
-            // Only this wave touches its tile, and a wave's LDS operations complete
-            // in program order, so last iteration's reads precede these writes.
-            unsigned char* vt = lds + wave * DEC_VBYTES;
-            // V tile -> LDS, transposed to [channel][key].
-    #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int item = lane + 64 * i;
-                const int kp = item >> 4, ch = item & 15;
-                const unsigned aw[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-                const unsigned bw[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
-    #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const unsigned lo = (e & 1) ? (aw[e >> 1] >> 16) : (aw[e >> 1] & 0xffffu);
-                    const unsigned hi = (e & 1) ? (bw[e >> 1] & 0xffff0000u) : (bw[e >> 1] << 16);
-                    *reinterpret_cast<unsigned*>(vt + (ch * 8 + e) * DEC_VROW + kp * 4) = lo | hi;
-                }
-            }
-            // S^T = K . Q^T for the two 16-key halves of the tile.
+            // S^T = K . Q^T for the two 16-key halves of the tile.  The waits the
+            // compiler emits for kreg also cover this tile's V copies, issued
+            // before its keys.
             f32x4 s[2];
     #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -197,14 +242,14 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                     s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[t][st]),
                                                                    qf[st], s[t], 0, 0, 0);
             }
-            if (it + 1 < DEC_ITERS) fetch(it + 1);
-            // The V^T tile is private to this wave and a wave's LDS accesses are
-            // performed in order, so ordering the stores before the loads below
-            // needs only a wavefront-scope fence, not a workgroup barrier (which
-            // would hold every wave to the slowest one each iteration).
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // The next tile: its values into the other LDS tile (last read by
+            // the products of tile it-1, complete before this iteration), then
+            // its keys into kreg.
+            if (it + 1 < DEC_ITERS) {
+                fetch_v(it + 1);
+                fetch_k(it + 1);
+            }
+            const unsigned char* vt = lds + wave * 2 * DEC_VBYTES + (it & 1) * DEC_VBYTES;
             if (!active) continue;
 
             // Mask positions past the chunk end; online softmax per head.
@@ -246,7 +291,7 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
             // O^T += V^T . P^T over 8 blocks of 16 channels.
     #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
-                bf16x8 vf = __builtin_bit_cast(bf16x8, ld16(vt + (blk * 16 + col) * DEC_VROW + grp * 16));
+                const bf16x8 vf = vfrag(vt, blk);
                 acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[blk], 0, 0, 0);
             }
         }
@@ -255,7 +300,7 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
         // inside it; idle waves carry m = -inf, l = 0, O = 0 and merge as nothing.
         lsum += __shfl_xor(lsum, 16);
         lsum += __shfl_xor(lsum, 32);
-        __syncthreads();   // every wave is done reading its V^T tile
+        __syncthreads();   // every wave is done reading its V tiles
         if (col_ok) {
             if (grp == 0) {
                 merge_m[wave][col] = mref;
@@ -289,7 +334,7 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                 st[DEC_D + 1] = l;
             }
         }
-        __syncthreads();   // the merge buffer is read before the next item's V^T tiles
+        __syncthreads();   // the merge buffer is read before the next item's V tiles
     }
 }
 
