@@ -463,7 +463,7 @@ def test_decode_rescale_stress(mode):
     compare(out.cpu().numpy(), ref, "bf16", case.name)
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 2), (16, 2), (32, 8), (8, 4)])
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (16, 2), (32, 8), (8, 4), (32, 2)])
 def test_decode_group_sizes(hq, hkv):
     case = W.DecodeCase("decode_g%d" % (hq // hkv), B=2, Hq=hq, Hkv=hkv, D=128, Lmin=500,
                         Lmax=2500, layer=1, seed=hq * 10 + hkv)
