@@ -35,6 +35,12 @@ def prefill_flops(case) -> float:
     return float(case.pairs()) * (4 * case.d + 2 * case.dv)
 
 
+def executed_prefill_flops(case) -> float:
+    """Matrix-core flops the fused kernel executes: per visible pair, both
+    d-long score dots and one dv-wide accumulation per map."""
+    return float(case.pairs()) * (4 * case.d + 4 * case.dv)
+
+
 def decode_bytes(case, lens) -> float:
     """Algorithmic HBM bytes: every visible K and V row once (bf16), plus q,
     lambda, lengths and the fp32 output."""
@@ -198,6 +204,13 @@ def main():
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
             "algorithmic_flops_per_launch": fp,
             "avg_launch_ms": round(pre_ms, 4),
+            # The exact single pass keeps one accumulator per map, so the
+            # matrix cores execute 2d + 2d + dv + dv = 4d + 4dv flop per pair
+            # (1.5x the algorithmic count at d = 64, dv = 128): the matrix-core
+            # utilisation beside the algorithmic fraction.
+            "executed_mfma_flops_per_launch": executed_prefill_flops(pcase),
+            "executed_mfma_frac": round(executed_prefill_flops(pcase) / (pre_ms * 1e-3) / 1e12
+                                        / PEAK_BF16_TFLOPS, 4),
         },
         "decode": {
             "bound": "hbm",
