@@ -183,6 +183,25 @@ def test_prefill_long_workloads_sampled(case):
     compare(got, ref, "bf16", case.name + " sampled")
 
 
+def test_prefill_longest_sequence_sampled():
+    # The longest context any workload here runs through the fused kernel (the
+    # noise-floor sweep's 256k), one head pair, the 64k workload's layer and
+    # norm: sampled rows at full size, including the last rows.
+    case = W.scaled_prefill(W.MULTI_NEEDLE_64K, N=262144, H=1)
+    say("bf16 prefill, multi-needle recipe at H=1 N=%d (sampled rows)" % case.N)
+    inp = W.make_prefill(case, device=DEV)
+    g = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 65535, 65536, case.N - 257, case.N - 256,
+                                      case.N - 2, case.N - 1], g.integers(0, case.N, 20)]))
+    lam_gpu = gpu_lambda(inp, case.layer)
+    out = run_prefill_gpu(case, inp, lam_gpu)
+    torch.cuda.synchronize()
+    got = out.reshape(-1, case.dv)[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    del out
+    ref = run_prefill_oracle(case, inp, lam_gpu.cpu().numpy(), rows=rows.astype(np.int64))
+    compare(got, ref, "bf16", "multi-needle recipe, H=1 N=%d, sampled" % case.N)
+
+
 # ---------------------------------------------------------------------------
 # V2-layout prefill: doubled query heads over shared K/V heads
 # ---------------------------------------------------------------------------
