@@ -8,24 +8,31 @@
 // query heads of a group; part 二 Step 2 for the operator).
 //
 // The cache is read exactly once, which makes the kernel HBM-bound:
-//  - split kernel: persistent, about two workgroups per CU.  The work items
-//    are the (sequence, KV head, chunk of DEC_CHUNK positions) triples that
-//    hold keys; every workgroup enumerates them from the lengths in the same
-//    order and takes every gridDim.x-th one, so the launch costs the same for
-//    any length mix (a grid over max_len would dispatch mostly empty
-//    workgroups).  One item streams its chunk of K_g and V_g for ALL Hq/Hkv
-//    query heads of the group (both heads of every pair).  Each of its 4 waves takes every
-//    4th 32-key tile of the chunk.  Scores come from v_mfma_f32_16x16x32_bf16
+//  - split kernel: about two workgroups per CU, each with an equal share of
+//    the keys.  The cached rows of all (sequence, KV head) segments, laid end
+//    to end (sequence-major, head-minor), are cut into gridDim.x contiguous
+//    ranges of one length R (a multiple of the 128 keys one loop step covers,
+//    at least DEC_RANGE_MIN), so every workgroup streams the same number of
+//    keys whatever the length mix; fixed chunks dealt round-robin leave the
+//    workgroups that draw one chunk more as the tail of the launch.  A
+//    workgroup takes its range as one piece per segment it touches; piece k
+//    of a segment is its k-th range, so a segment has at most
+//    ceil(max_len / DEC_RANGE_MIN) + 1 pieces.  One piece streams its rows of
+//    K_g and V_g for ALL Hq/Hkv query heads of the group (both heads of every
+//    pair).  Each of its 4 waves takes every 4th 32-key tile of the piece.  Scores come from v_mfma_f32_16x16x32_bf16
 //    as S^T = K . Q^T (keys x query heads, the 16 columns padded with zero
 //    heads); probabilities go from registers into O^T += V^T . P^T.  Each V
 //    tile is copied from global memory straight into one of the wave's two
 //    LDS tiles (buffer loads that write LDS, one tile ahead) and its V^T
 //    fragments are read with the transpose load.  Each head keeps
 //    its own running maximum / normaliser / accumulator; the waves' states are
-//    merged in LDS and one partial state (O, m, l) per head and split is
+//    merged in LDS and one partial state (O, m, l) per head and piece is
 //    written to the workspace.
-//  - merge kernel: grid (pair, sequence).  Merges the splits of both heads of
-//    a pair by log-sum-exp weights in a fixed order (deterministic), then
+//    The workgroup that streams the last piece of a segment also writes the
+//    segment's piece count.
+//  - merge kernel: grid (pair, sequence).  Merges the pieces of the pair's
+//    segment for both heads of the pair by log-sum-exp weights in a fixed
+//    order (deterministic for a given grid), then
 //    combines the two maps with lambda and optionally applies the per-head
 //    RMS norm.
 //
@@ -51,8 +58,8 @@ constexpr int DEC_D = 128;             // head width
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
 constexpr int DEC_TILE = 32;           // keys per wave iteration
-constexpr int DEC_CHUNK = 4096;        // keys per work item (one split)
-constexpr int DEC_ITERS = DEC_CHUNK / (DEC_TILE * DEC_WAVES);
+constexpr int DEC_STEP = DEC_TILE * DEC_WAVES;   // keys per loop step of a workgroup
+constexpr int DEC_RANGE_MIN = 4096;    // shortest key range per workgroup
 constexpr int DEC_GROUP_MAX = 16;      // query heads per KV head that fit the MFMA columns
 constexpr int DEC_VROWB = DEC_D * 2;            // bytes per cached V row
 constexpr int DEC_VBYTES = DEC_TILE * DEC_VROWB; // one V tile, token-major (8 KB)
@@ -113,11 +120,24 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
 // 8 consecutive keys per lane group: the B operand of the next product.
 __device__ __forceinline__ int slot_key(int rho, int t) { return (rho >> 2) * 8 + t * 4 + (rho & 3); }
 
+// Length of sequence bb, 0 when outside [1, max_len] (such a sequence has no
+// keys and its outputs are zeros).
+__device__ __forceinline__ int valid_len(const int32_t* seq_lens, int bb, int max_len) {
+    const int Lb = seq_lens[bb];
+    return (Lb < 1 || Lb > max_len) ? 0 : Lb;
+}
+// Keys per workgroup range for `total` keys over `nranges` ranges.
+__device__ __forceinline__ int64_t range_len(int64_t total, int nranges) {
+    int64_t r = (total + nranges - 1) / nranges;
+    r = (r + DEC_STEP - 1) / DEC_STEP * DEC_STEP;
+    return r < DEC_RANGE_MIN ? DEC_RANGE_MIN : r;
+}
+
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens, int B,
                     int Hq, int Hkv, int max_len, int max_splits, float* __restrict__ ws,
-                    int qhalf, float c) {
+                    int* __restrict__ piece_count, int qhalf, float c) {
     // Two V tiles per wave during the stream; reused as the wave-merge buffer.
     __shared__ __attribute__((aligned(16))) unsigned char lds[DEC_WAVES * 2 * DEC_VBYTES];
     __shared__ float merge_m[DEC_WAVES][DEC_GROUP_MAX];
@@ -134,30 +154,31 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
     const int G = Hq / Hkv;         // query heads in this KV group
     const bool col_ok = col < G;
 
-    // Chunks of sequence b (0 for an invalid length: the merge kernel then
-    // writes zeros).  Items are numbered sequence by sequence, KV head by KV
-    // head, chunk by chunk.
-    auto nchunks = [&](int bb) -> int {
-        const int Lb = seq_lens[bb];
-        return (Lb < 1 || Lb > max_len) ? 0 : (Lb + DEC_CHUNK - 1) / DEC_CHUNK;
-    };
-    int total = 0;
-    for (int bb = 0; bb < B; ++bb) total += nchunks(bb) * Hkv;
-    int b = 0, base = 0, nb = B > 0 ? nchunks(0) : 0;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        // Items only grow, so the sequence pointer only moves forward; item <
-        // total keeps it below B.
-        while (item >= base + nb * Hkv) {
-            base += nb * Hkv;
-            ++b;
-            nb = nchunks(b);
-        }
-        const int g = (item - base) / nb;
-        const int split = (item - base) % nb;
-        const int L = seq_lens[b];
-        const int c0 = split * DEC_CHUNK;
-        const int cend = min(L, c0 + DEC_CHUNK);
-
+    // This workgroup's key range [r0, r1) (uniform).
+    int64_t total = 0;
+    for (int bb = 0; bb < B; ++bb) total += (int64_t)valid_len(seq_lens, bb, max_len) * Hkv;
+    const int64_t R = range_len(total, gridDim.x);
+    const int64_t r0 = (int64_t)blockIdx.x * R;
+    if (r0 >= total) return;
+    const int64_t r1 = min(total, r0 + R);
+    // The segment holding r0: sequence b (keys from base on), head g.  The walk
+    // stops at a sequence with keys because r0 < total.
+    int b = 0, L = valid_len(seq_lens, 0, max_len);
+    int64_t base = 0;
+    while (base + (int64_t)L * Hkv <= r0) {
+        base += (int64_t)L * Hkv;
+        ++b;
+        L = valid_len(seq_lens, b, max_len);
+    }
+    int g = (int)((r0 - base) / L);
+    int64_t seg0 = base + (int64_t)g * L;   // first key of segment (b, g)
+    for (int64_t pos = r0; pos < r1;) {
+        // Piece: positions c0 .. cend-1 of segment (b, g); it is the
+        // (blockIdx.x - seg0/R)-th range that touches the segment.
+        const int c0 = (int)(pos - seg0);
+        const int cend = (int)min((int64_t)L, r1 - seg0);
+        const int split = (int)(blockIdx.x - seg0 / R);
+        const int n_it = (cend - c0 + DEC_STEP - 1) / DEC_STEP;
         const int64_t kv0 = ((int64_t)b * Hkv + g) * max_len;   // row of position 0
         // c = log2(e) / sqrt(dot length), from the host.
 
@@ -198,7 +219,7 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
         const unsigned vlds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds + wave * 2 * DEC_VBYTES));
         auto fetch_v = [&](int it) {
             const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
-            // Rows past the chunk end read as zeros (their probabilities are 0).
+            // Rows past the piece end read as zeros (their probabilities are 0).
             const int rows = max(0, min(DEC_TILE, cend - kb));
             const i32x4 r = make_rsrc(vc + (kv0 + kb) * DEC_D, rows * DEC_VROWB);
             const unsigned dst = vlds0 + (unsigned)((it & 1) * DEC_VBYTES);
@@ -227,7 +248,7 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
 
         fetch_v(0);
         fetch_k(0);
-        for (int it = 0; it < DEC_ITERS; ++it) {
+        for (int it = 0; it < n_it; ++it) {
             const int kb = c0 + (it * DEC_WAVES + wave) * DEC_TILE;
             const bool active = kb < cend;
             // S^T = K . Q^T for the two 16-key halves of the tile.  The waits the
@@ -245,14 +266,14 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
             // The next tile: its values into the other LDS tile (last read by
             // the products of tile it-1, complete before this iteration), then
             // its keys into kreg.
-            if (it + 1 < DEC_ITERS) {
+            if (it + 1 < n_it) {
                 fetch_v(it + 1);
                 fetch_k(it + 1);
             }
             const unsigned char* vt = lds + wave * 2 * DEC_VBYTES + (it & 1) * DEC_VBYTES;
             if (!active) continue;
 
-            // Mask positions past the chunk end; online softmax per head.
+            // Mask positions past the piece end; online softmax per head.
             float sv[8];
     #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -296,7 +317,7 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
             }
         }
 
-        // Every wave saw at least one key of the chunk only if its first tile was
+        // Every wave saw at least one key of the piece only if its first tile was
         // inside it; idle waves carry m = -inf, l = 0, O = 0 and merge as nothing.
         lsum += __shfl_xor(lsum, 16);
         lsum += __shfl_xor(lsum, 32);
@@ -334,11 +355,25 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                 st[DEC_D + 1] = l;
             }
         }
-        __syncthreads();   // the merge buffer is read before the next item's V tiles
+        if (cend == L && tid == 0) piece_count[b * Hkv + g] = split + 1;
+        __syncthreads();   // the merge buffer is read before the next piece's V tiles
+        // Next segment (a piece that ends before r1 ends its segment); sequences
+        // without keys are skipped, and one with keys follows because pos < r1.
+        pos = seg0 + cend;
+        if (pos < r1) {
+            seg0 += L;
+            if (++g == Hkv) {
+                g = 0;
+                do {
+                    ++b;
+                    L = valid_len(seq_lens, b, max_len);
+                } while (L == 0);
+            }
+        }
     }
 }
 
-// Merge the splits of both heads of a pair and combine them with lambda.
+// Merge the pieces of both heads of a pair and combine them with lambda.
 // 256 threads: thread (m, ch) owns channel ch of head 2p+m.  The split maxima
 // are reduced once through LDS; each thread then sums its channel over the
 // splits with independent loads (unrolled), so the kernel is not a chain of
@@ -347,8 +382,9 @@ constexpr int MERGE_THREADS = 2 * DEC_D;
 constexpr int MERGE_LDS_SPLITS = 1024;   // splits whose weights are cached in LDS
 
 __global__ void __launch_bounds__(MERGE_THREADS)
-decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict__ seq_lens, int Hq,
-                    int max_len, int max_splits, const float* __restrict__ lambda,
+decode_merge_kernel(const float* __restrict__ ws, const int* __restrict__ piece_count,
+                    const int32_t* __restrict__ seq_lens, int Hq, int Hkv, int max_len,
+                    int max_splits, const float* __restrict__ lambda,
                     float* __restrict__ out, int rmsnorm, float eps, float norm_scale,
                     const float* __restrict__ norm_weight) {
     const int p = blockIdx.x;
@@ -363,10 +399,11 @@ decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict__ se
         if (tid < DEC_D) o[tid] = 0.f;
         return;
     }
-    const int nsplit = (L + DEC_CHUNK - 1) / DEC_CHUNK;
     __shared__ float w_lds[2][MERGE_LDS_SPLITS];
     __shared__ float red[2][MERGE_THREADS / 64];
     __shared__ float res[DEC_D];
+    // Pieces of segment (b, g), written by the split kernel.
+    const int nsplit = min(piece_count[b * Hkv + (2 * p) / (Hq / Hkv)], max_splits);
     const float* st = ws + ((int64_t)b * Hq + 2 * p + m) * max_splits * DEC_STATE;
 
     // Maximum of the split maxima of this thread's head (both heads at once:
@@ -410,16 +447,24 @@ decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict__ se
 
 bool decode_supported(int D) { return D == DEC_D; }
 
-int decode_max_splits(int max_len) { return (max_len + DEC_CHUNK - 1) / DEC_CHUNK; }
+// Pieces per segment: a segment of L <= max_len keys meets at most
+// ceil(L / R) + 1 ranges of R >= DEC_RANGE_MIN keys.
+int decode_max_splits(int max_len) { return (max_len + DEC_RANGE_MIN - 1) / DEC_RANGE_MIN + 1; }
 
-size_t decode_workspace_floats(int B, int Hq, int D, int max_len) {
-    (void)D;
+// Partial states [B][Hq][max_splits][DEC_STATE], then one piece count per
+// (sequence, KV head) (at most Hq of them per sequence).
+static size_t decode_state_floats(int B, int Hq, int max_len) {
     return (size_t)B * Hq * decode_max_splits(max_len) * DEC_STATE;
 }
+size_t decode_workspace_floats(int B, int Hq, int D, int max_len) {
+    (void)D;
+    return decode_state_floats(B, Hq, max_len) + (size_t)B * Hq;
+}
 
-// Workgroups of the persistent split kernel: two per CU (its register use
-// allows two per CU), never more than there can be items.
-static int decode_split_grid(int B, int Hkv, int S) {
+// Workgroups (= key ranges) of the split kernel: two per CU (its register
+// use allows two per CU), never more than ranges of DEC_RANGE_MIN keys can be
+// non-empty.
+static int decode_split_grid(int B, int Hkv, int max_len) {
     // CU count per device, cached (a repeated first query is harmless).
     static std::atomic<int> cus[64];
     int dev = 0;
@@ -430,24 +475,25 @@ static int decode_split_grid(int B, int Hkv, int S) {
             n = 256;
         if (dev >= 0 && dev < 64) cus[dev].store(n, std::memory_order_relaxed);
     }
-    const int64_t items = (int64_t)B * Hkv * S;
+    const int64_t ranges = (int64_t)B * Hkv * ((max_len + DEC_RANGE_MIN - 1) / DEC_RANGE_MIN);
     const int64_t want = 2 * (int64_t)n;
-    return (int)(items < want ? items : want);
+    return (int)(ranges < want ? ranges : want);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (a.D != DEC_D || a.Hq / a.Hkv > DEC_GROUP_MAX) return hipErrorInvalidValue;
     const int S = decode_max_splits(a.max_len);
     const float c = 1.4426950408889634f / sqrtf((float)(a.qhalf > 0 ? a.qhalf : DEC_D));
-    const int grid = decode_split_grid(a.B, a.Hkv, S);
+    const int grid = decode_split_grid(a.B, a.Hkv, a.max_len);
+    int* counts = reinterpret_cast<int*>(a.workspace + decode_state_floats(a.B, a.Hq, a.max_len));
     if (grid > 0)
         hipLaunchKernelGGL(decode_split_kernel, dim3(grid), dim3(DEC_THREADS), 0, stream,
                            (const __bf16*)a.q, (const __bf16*)a.k_cache, (const __bf16*)a.v_cache,
-                           a.seq_lens, a.B, a.Hq, a.Hkv, a.max_len, S, a.workspace, a.qhalf, c);
+                           a.seq_lens, a.B, a.Hq, a.Hkv, a.max_len, S, a.workspace, counts, a.qhalf, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq / 2, a.B), dim3(MERGE_THREADS), 0, stream,
-                       a.workspace, a.seq_lens, a.Hq, a.max_len, S, a.lambda, a.out, a.rmsnorm,
+                       a.workspace, counts, a.seq_lens, a.Hq, a.Hkv, a.max_len, S, a.lambda, a.out, a.rmsnorm,
                        a.eps, a.norm_scale, a.norm_weight);
     return hipGetLastError();
 }
