@@ -151,7 +151,9 @@ diffattn_status_t diffattn_combine(const float* o1, const float* o2, const float
 
 /*
  * Bytes of device workspace diffattn_decode needs for these sizes (partial
- * softmax states of every KV split).  Returns 0 for invalid sizes.
+ * softmax states of every KV piece, ceil(max_len/4096)+1 per sequence and
+ * query head, and a piece count per sequence and KV head).  Returns 0 for
+ * invalid sizes.
  */
 size_t diffattn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len);
 
@@ -182,7 +184,8 @@ diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void
 
 /*
  * Bytes of device workspace diffattn_decode_v1 needs (two partial softmax
- * states, one per map, per head and KV split).  Returns 0 for invalid sizes.
+ * states, one per map, per head and KV piece, and a piece count per head).
+ * Returns 0 for invalid sizes.
  */
 size_t diffattn_decode_v1_workspace_bytes(int B, int H, int max_len);
 
