@@ -451,11 +451,11 @@ def test_decode_ragged_lengths(lens):
 
 @pytest.mark.parametrize("mode", ["wide", "growing"])
 def test_decode_rescale_stress(mode):
-    """Decode over several chunks per sequence with logits far wider than the
+    """Decode over several pieces per sequence with logits far wider than the
     workload's: "wide" scales the queries by 6; "growing" adds (j/L) * 30
     sqrt(D) * u to cached key j along a fixed unit direction u, so a head's
     scores drift by up to about 30 across the sequence (new maxima inside and
-    across chunks, or underflowing probabilities), which exercises the lazy
+    across pieces, or underflowing probabilities), which exercises the lazy
     rescale in the split kernel and the log-sum-exp weights of the merge."""
     lens = [9000, 4097, 2500, 1]
     case = W.DecodeCase("decode_stress_%s" % mode, B=len(lens), Hq=8, Hkv=2, D=128,
@@ -504,13 +504,40 @@ def test_decode_invalid_device_length_gives_zeros():
     compare(out[:1].cpu().numpy(), ref, "bf16", "decode valid row")
 
 
+def test_decode_many_short_sequences_in_one_range():
+    # 300 sequences of 1 .. 40 keys over 8 KV heads: about 49k keys in about
+    # 12 ranges of the minimum length, so each workgroup walks some 200
+    # segments (whole ones, plus a cut one at each end of its range) and skips
+    # the sequences without keys.
+    B, max_len = 300, 40
+    case = W.DecodeCase("decode_short", B=B, Hq=16, Hkv=8, D=128, Lmin=1, Lmax=max_len, layer=2,
+                        seed=91)
+    say("decode %d short sequences in one key range" % B)
+    inp = W.make_decode(case, device=DEV)
+    lens = torch.randint(1, max_len + 1, (B,), generator=torch.Generator().manual_seed(12),
+                         dtype=torch.int32)
+    bad = [0, 1, 150, 299]
+    for i, v in zip(bad, [0, max_len + 1, -1, 0]):
+        lens[i] = v
+    inp["seq_lens"] = lens.to(DEV)
+    lam = gpu_lambda(inp, case.layer)
+    out = api.diffattn_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[bad]).item() == 0
+    good = [b for b in range(B) if b not in bad]
+    ref = oracle.decode(inp["q"][good].cpu(), inp["k_cache"][good].cpu(), inp["v_cache"][good].cpu(),
+                        lens[good].numpy(), lam.cpu().numpy())
+    compare(out[good].cpu().numpy(), ref, "bf16", case.name)
+
+
 def test_decode_many_items_with_invalid_lengths():
-    # More (sequence, KV head, chunk) items than workgroups, so every
-    # workgroup strides over several, with out-of-range lengths in between.
+    # Key ranges of about 6k keys over segments of 1 .. 12288: most ranges
+    # cover pieces of several segments and skip the out-of-range lengths in
+    # between.
     B, max_len = 64, 12288
     case = W.DecodeCase("decode_items", B=B, Hq=16, Hkv=8, D=128, Lmin=1, Lmax=max_len, layer=3,
                         seed=77)
-    say("decode %d sequences, several chunks each, invalid lengths interleaved" % B)
+    say("decode %d sequences, several pieces each, invalid lengths interleaved" % B)
     inp = W.make_decode(case, device=DEV)
     lens = torch.randint(1, max_len + 1, (B,), generator=torch.Generator().manual_seed(11),
                          dtype=torch.int32)
