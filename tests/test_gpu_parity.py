@@ -504,6 +504,39 @@ def test_decode_invalid_device_length_gives_zeros():
     compare(out[:1].cpu().numpy(), ref, "bf16", "decode valid row")
 
 
+@pytest.mark.parametrize("layout", ["v2", "v1"])
+def test_decode_bitwise_repeatable_over_stale_workspace(layout):
+    # Two calls on one workspace, the second after the workspace was filled
+    # with 0xFF bytes (NaN states, piece counts of -1): every call rewrites
+    # every state and count the merge reads, and the fixed merge order makes
+    # the output bitwise identical.
+    lens = torch.tensor([20000, 4096, 1, 9001, 12345, 8192], dtype=torch.int32)
+    if layout == "v2":
+        case = W.DecodeCase("decode_repeat", B=len(lens), Hq=32, Hkv=8, D=128, Lmin=1,
+                            Lmax=20000, layer=4, seed=1234)
+        inp = W.make_decode(case, device=DEV)
+        nbytes = api.diffattn_decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.D, case.Lmax)
+    else:
+        case = W.V1DecodeCase("decode_v1_repeat", B=len(lens), H=8, d=64, dv=128, Lmin=1,
+                              Lmax=20000, layer=4, seed=1235)
+        inp = W.make_decode_v1(case, device=DEV)
+        nbytes = api.diffattn_decode_v1_workspace_bytes(case.B, case.H, case.Lmax)
+    say("decode %s repeatability over a stale workspace" % layout)
+    inp["seq_lens"] = lens.to(DEV)
+    lam = gpu_lambda(inp, case.layer)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    run = (lambda: api.diffattn_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam,
+                                       workspace=ws)) if layout == "v2" else \
+          (lambda: api.diffattn_decode_v1(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam,
+                                          workspace=ws))
+    first = run().clone()
+    ws.fill_(0xFF)
+    second = run()
+    torch.cuda.synchronize()
+    assert torch.isfinite(first).all()
+    assert torch.equal(first, second)
+
+
 def test_decode_many_short_sequences_in_one_range():
     # 300 sequences of 1 .. 40 keys over 8 KV heads: about 49k keys in about
     # 12 ranges of the minimum length, so each workgroup walks some 200
