@@ -189,6 +189,13 @@ def test_decode_v1_workspace_size(lib):
 def test_decode_workspace_size(lib):
     n = api.diffattn_decode_workspace_bytes(32, 32, 8, 128, 65536)
     assert n >= 32 * 32 * 130 * 4 and n % 4 == 0
+    # Per (sequence, query head): up to ceil(max_len / 4096) + 1 partial states
+    # of D + 2 floats (one per key range that meets the segment); then one
+    # piece count per (sequence, query head) slot.
+    for B, Hq, max_len in ((32, 32, 65536), (1, 2, 1), (3, 8, 4097)):
+        pieces = -(-max_len // 4096) + 1
+        assert api.diffattn_decode_workspace_bytes(B, Hq, 2, 128, max_len) == \
+            (B * Hq * pieces * 130 + B * Hq) * 4
     assert api.diffattn_decode_workspace_bytes(0, 32, 8, 128, 65536) == 0
 
 
