@@ -93,6 +93,24 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+def _same_device(*named):
+    """All tensors on one device (the kernels address them from one GPU)."""
+    dev = None
+    for t, name in named:
+        if t is None:
+            continue
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, expected %s like the other tensors" % (name, t.device, dev))
+
+
+def _check_lambda(lam, n: int, what: str = "H"):
+    if not isinstance(lam, torch.Tensor) or lam.dtype != torch.float32 or lam.numel() != n \
+            or not lam.is_contiguous():
+        raise ValueError("lambda must be a contiguous fp32 tensor of %s = %d entries" % (what, n))
+
+
 def _token_stride(t: torch.Tensor, name: str) -> int:
     """ld of a [B, H, N, w] tensor laid out as [B][H][N][ld] with unit channel stride."""
     if t.dim() != 4:
@@ -121,9 +139,14 @@ def diffattn_lambda(lq1, lk1, lq2, lk2, layer: int, out=None, stream=None) -> to
     for t in (lq1, lk1, lq2, lk2):
         if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != lq1.shape:
             raise ValueError("lq1, lk1, lq2, lk2 must be contiguous fp32 tensors of one shape")
+    if lq1.dim() not in (1, 2):
+        raise ValueError("lq1, lk1, lq2, lk2 must be [H, dim] or [dim]")
     H, dim = (1, lq1.shape[0]) if lq1.dim() == 1 else lq1.shape
     if out is None:
         out = torch.empty(H, dtype=torch.float32, device=lq1.device)
+    if out.dtype != torch.float32 or out.numel() != H or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor of H = %d entries" % H)
+    _same_device((lq1, "lq1"), (lk1, "lk1"), (lq2, "lq2"), (lk2, "lk2"), (out, "out"))
     _check(lib.diffattn_lambda(_ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), H, dim, int(layer),
                                _ptr(out), _stream(stream)))
     return out
@@ -159,8 +182,16 @@ def diffattn_prefill(q1, q2, k1, k2, v, lam, *, causal: bool = True, rmsnorm: bo
     ldv = _token_stride(v, "v")
     if ldq != ldq2 or ldk != ldk2:
         raise ValueError("q1/q2 and k1/k2 must share their token strides")
+    _check_lambda(lam, H)
+    if rmsnorm and norm_weight is not None and (norm_weight.dtype != torch.float32
+                                                or norm_weight.numel() != dv):
+        raise ValueError("norm_weight must be fp32 [dv]")
     if out is None:
         out = torch.empty((B, H, N, dv), dtype=torch.float32, device=q1.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, dv) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [B, H, N, dv]")
+    _same_device((q1, "q1"), (q2, "q2"), (k1, "k1"), (k2, "k2"), (v, "v"), (lam, "lambda"),
+                 (norm_weight if rmsnorm else None, "norm_weight"), (out, "out"))
     _check(lib.diffattn_prefill(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), ldq, ldk, ldv, dt,
                                 B, H, N, d, dv, int(bool(causal)), _ptr(lam), int(bool(rmsnorm)),
                                 float(eps), float(norm_scale), _ptr(norm_weight), _ptr(out),
@@ -195,10 +226,12 @@ def diffattn_prefill_v2(q, k, v, lam, *, causal: bool = True, out=None, stream=N
     Hkv = k.shape[1]
     if k.shape != (B, Hkv, N, D) or v.shape != (B, Hkv, N, D):
         raise ValueError("k and v must be [B, Hkv, N, D]")
-    if lam.dtype != torch.float32 or lam.numel() != Hq // 2:
-        raise ValueError("lambda must be fp32 [Hq/2]")
+    _check_lambda(lam, Hq // 2, "Hq/2")
     if out is None:
         out = torch.empty((B, Hq // 2, N, D), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Hq // 2, N, D) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [B, Hq/2, N, D]")
+    _same_device((q, "q"), (k, "k"), (v, "v"), (lam, "lambda"), (out, "out"))
     _check(lib.diffattn_prefill_v2(_ptr(q), _ptr(k), _ptr(v), dtype, B, Hq, Hkv, N, D,
                                    1 if causal else 0, _ptr(lam), _ptr(out), _stream(stream)))
     return out
@@ -214,9 +247,14 @@ def diffattn_attention(q, k, v, *, causal: bool = True, out=None, stream=None) -
             raise ValueError("%s must be bf16" % name)
     B, H, N, d = q.shape
     dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape[:3]) != (B, H, N):
+        raise ValueError("k must be [B, H, N, d] like q and v [B, H, N, dv]")
     ldq, ldk, ldv = _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v")
     if out is None:
         out = torch.empty((B, H, N, dv), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, dv) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [B, H, N, dv]")
+    _same_device((q, "q"), (k, "k"), (v, "v"), (out, "out"))
     _check(lib.diffattn_attention(_ptr(q), _ptr(k), _ptr(v), ldq, ldk, ldv, DIFFATTN_BF16, B, H, N,
                                   d, dv, 1 if causal else 0, _ptr(out), _stream(stream)))
     return out
@@ -231,8 +269,16 @@ def diffattn_combine(o1, o2, lam, *, rmsnorm: bool = False, eps: float = 1e-5,
         if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != o1.shape:
             raise ValueError("%s must be contiguous fp32 of one shape" % name)
     B, H, N, dv = o1.shape
+    _check_lambda(lam, H)
     if out is None:
         out = torch.empty_like(o1)
+    if out.dtype != torch.float32 or out.shape != o1.shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 of o1's shape")
+    if rmsnorm and norm_weight is not None and (norm_weight.dtype != torch.float32
+                                                or norm_weight.numel() != dv):
+        raise ValueError("norm_weight must be fp32 [dv]")
+    _same_device((o1, "o1"), (o2, "o2"), (lam, "lambda"),
+                 (norm_weight if rmsnorm else None, "norm_weight"), (out, "out"))
     _check(lib.diffattn_combine(_ptr(o1), _ptr(o2), _ptr(lam), B, H, N, dv, 1 if rmsnorm else 0,
                                 eps, norm_scale, _ptr(norm_weight), _ptr(out), _stream(stream)))
     return out
@@ -251,18 +297,27 @@ def diffattn_decode(q, k_cache, v_cache, seq_lens, lam, *, workspace=None, out=N
     least diffattn_decode_workspace_bytes(...) bytes.
     """
     lib = load_library()
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be contiguous bf16" % name)
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and the caches [B, Hkv, max_len, D]")
     B, Hq, D = q.shape
     _, Hkv, max_len, _ = k_cache.shape
-    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
-    if seq_lens.dtype != torch.int32 or lam.dtype != torch.float32:
-        raise ValueError("seq_lens must be int32 and lambda fp32")
+    if tuple(k_cache.shape) != (B, Hkv, max_len, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [B, Hkv, max_len, D] for q [B, Hq, D]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of B = %d entries" % B)
+    _check_lambda(lam, Hq // 2, "Hq/2")
     need = diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, Hq // 2, D), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Hq // 2, D) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [B, Hq/2, D]")
+    _same_device((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens"),
+                 (lam, "lambda"), (workspace, "workspace"), (out, "out"))
     _check(lib.diffattn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv,
                                D, max_len, _ptr(lam), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _ptr(out),
@@ -292,13 +347,22 @@ def diffattn_decode_v1(q, k_cache, v_cache, seq_lens, lam, *, rmsnorm: bool = Tr
             raise ValueError("%s must be contiguous bf16" % name)
     if k_cache.shape != (B, H, max_len, d2) or v_cache.shape[:3] != (B, H, max_len):
         raise ValueError("cache shapes must be [B, H, max_len, 2d] and [B, H, max_len, dv]")
-    if seq_lens.dtype != torch.int32 or lam.dtype != torch.float32:
-        raise ValueError("seq_lens must be int32 and lambda fp32")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of B = %d entries" % B)
+    _check_lambda(lam, H)
+    if rmsnorm and norm_weight is not None and (norm_weight.dtype != torch.float32
+                                                or norm_weight.numel() != dv):
+        raise ValueError("norm_weight must be fp32 [dv]")
     need = diffattn_decode_v1_workspace_bytes(B, H, max_len)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, H, dv) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [B, H, dv]")
+    _same_device((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens"),
+                 (lam, "lambda"), (norm_weight if rmsnorm else None, "norm_weight"),
+                 (workspace, "workspace"), (out, "out"))
     _check(lib.diffattn_decode_v1(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, H,
                                   d2 // 2, dv, max_len, _ptr(lam), 1 if rmsnorm else 0, eps,
                                   norm_scale, _ptr(norm_weight), _ptr(workspace),

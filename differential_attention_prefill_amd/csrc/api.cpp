@@ -49,6 +49,15 @@ diffattn_status_t check_device(const void* p, const char* name) {
     return DIFFATTN_OK;
 }
 
+// The bf16 kernels address a tile of 64 token rows with 32-bit byte offsets
+// (copy offsets, tile strides and buffer extents of up to 64 * ld * 2
+// bytes), so every token stride must keep 64 rows below 2^31 bytes.
+constexpr int64_t BF16_MAX_LD = ((int64_t)1 << 31) / (64 * 2) - 1;
+
+bool bf16_ld_ok(int64_t ldq, int64_t ldk, int64_t ldv) {
+    return ldq <= BF16_MAX_LD && ldk <= BF16_MAX_LD && ldv <= BF16_MAX_LD;
+}
+
 diffattn_status_t hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
     return fail(DIFFATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -85,7 +94,7 @@ diffattn_status_t diffattn_lambda(const float* lq1, const float* lk1, const floa
 
 diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k1, const void* k2,
                                    const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
-                                   diffattn_dtype_t dtype, int B, int H, int N, int d, int dv,
+                                   int dtype, int B, int H, int N, int d, int dv,
                                    int causal, const float* lambda, int rmsnorm, float eps,
                                    float norm_scale, const float* norm_weight, float* out,
                                    void* stream) {
@@ -95,7 +104,7 @@ diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
                     "diffattn_prefill: B=%d H=%d N=%d d=%d dv=%d must be >= 1", B, H, N, d, dv);
     if (dtype != DIFFATTN_FP32 && dtype != DIFFATTN_BF16)
-        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: unknown dtype %d", (int)dtype);
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: unknown dtype %d", dtype);
     if (ldq < d || ldk < d || ldv < dv)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
                     "diffattn_prefill: strides ldq=%lld ldk=%lld ldv=%lld below widths d=%d dv=%d",
@@ -119,6 +128,10 @@ diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k
     if (!supported)
         return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_prefill: (d=%d, dv=%d) not built for %s", d,
                     dv, dtype == DIFFATTN_BF16 ? "bf16" : "fp32");
+    if (dtype == DIFFATTN_BF16 && !bf16_ld_ok(ldq, ldk, ldv))
+        return fail(DIFFATTN_ERR_UNSUPPORTED,
+                    "diffattn_prefill: bf16 token strides must be at most %lld elements",
+                    (long long)BF16_MAX_LD);
     if ((int64_t)B * H * N > (int64_t)1 << 40)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: B*H*N too large");
     for (int i = 0; i < 7; ++i) {
@@ -148,7 +161,7 @@ diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k
 }
 
 diffattn_status_t diffattn_prefill_v2(const void* q, const void* k, const void* v,
-                                      diffattn_dtype_t dtype, int B, int Hq, int Hkv, int N, int D,
+                                      int dtype, int B, int Hq, int Hkv, int N, int D,
                                       int causal, const float* lambda, float* out, void* stream) {
     if (!q || !k || !v || !lambda || !out)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill_v2: null pointer");
@@ -159,7 +172,7 @@ diffattn_status_t diffattn_prefill_v2(const void* q, const void* k, const void* 
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
                     "diffattn_prefill_v2: Hq=%d must be a multiple of 2*Hkv=%d", Hq, 2 * Hkv);
     if (dtype != DIFFATTN_FP32 && dtype != DIFFATTN_BF16)
-        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill_v2: unknown dtype %d", (int)dtype);
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill_v2: unknown dtype %d", dtype);
     const int esize = dtype == DIFFATTN_BF16 ? 2 : 4;
     if ((D * esize) % 16)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
@@ -206,7 +219,7 @@ diffattn_status_t diffattn_prefill_v2(const void* q, const void* k, const void* 
 }
 
 diffattn_status_t diffattn_attention(const void* q, const void* k, const void* v, int64_t ldq,
-                                     int64_t ldk, int64_t ldv, diffattn_dtype_t dtype, int B,
+                                     int64_t ldk, int64_t ldv, int dtype, int B,
                                      int H, int N, int d, int dv, int causal, float* out,
                                      void* stream) {
     if (!q || !k || !v || !out)
@@ -230,6 +243,10 @@ diffattn_status_t diffattn_attention(const void* q, const void* k, const void* v
                         names[i]);
     if (!diffattn::attention_pp_supported(d, dv))
         return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_attention: (d=%d, dv=%d) not built", d, dv);
+    if (!bf16_ld_ok(ldq, ldk, ldv))
+        return fail(DIFFATTN_ERR_UNSUPPORTED,
+                    "diffattn_attention: bf16 token strides must be at most %lld elements",
+                    (long long)BF16_MAX_LD);
     if ((int64_t)B * H * N > (int64_t)1 << 40)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_attention: B*H*N too large");
     for (int i = 0; i < 4; ++i) {
@@ -413,7 +430,7 @@ diffattn_status_t diffattn_decode_v1(const void* q, const void* k_cache, const v
     return hip_status(diffattn::launch_decode(a, (hipStream_t)stream), "diffattn_decode_v1 launch");
 }
 
-const char* diffattn_status_string(diffattn_status_t status) {
+const char* diffattn_status_string(int status) {
     switch (status) {
         case DIFFATTN_OK: return "ok";
         case DIFFATTN_ERR_INVALID_ARGUMENT: return "invalid argument";

@@ -26,6 +26,8 @@
  *    error no kernel is launched and no output is touched; the call returns a
  *    status code and diffattn_last_error() (thread-local) describes it.
  *  - Element strides are counted in elements of the tensor's own type.
+ *  - Element types are passed as an int holding a diffattn_dtype_t value;
+ *    any other value is rejected with INVALID_ARGUMENT.
  *  - No C++ exception crosses this interface.
  */
 #ifndef DIFFATTN_H_
@@ -92,12 +94,14 @@ diffattn_status_t diffattn_lambda(const float* lq1, const float* lk1, const floa
  * norm_scale = 1 - lambda_init for the V1 head normalisation.
  * Supported: BF16 with (d, dv) in {(64,128), (64,64), (32,64), (128,128)};
  * FP32 with d in {32, 64, 128} and dv in {64, 128}.  Other shapes return
- * UNSUPPORTED.  Pointers must be 16-byte aligned and ld*sizeof(elem) a
+ * UNSUPPORTED.  BF16 token strides ldq, ldk, ldv above 2^24 - 1 elements
+ * also return UNSUPPORTED (the kernels address 64-row tiles with 32-bit byte
+ * offsets).  Pointers must be 16-byte aligned and ld*sizeof(elem) a
  * multiple of 16 (INVALID_ARGUMENT otherwise).  B, H, N >= 1.
  */
 diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k1,
                                    const void* k2, const void* v, int64_t ldq, int64_t ldk,
-                                   int64_t ldv, diffattn_dtype_t dtype, int B, int H, int N,
+                                   int64_t ldv, int dtype, int B, int H, int N,
                                    int d, int dv, int causal, const float* lambda, int rmsnorm,
                                    float eps, float norm_scale, const float* norm_weight,
                                    float* out, void* stream);
@@ -119,7 +123,7 @@ diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k
  * a multiple of 16 (INVALID_ARGUMENT otherwise).  Asynchronous on stream.
  */
 diffattn_status_t diffattn_prefill_v2(const void* q, const void* k, const void* v,
-                                      diffattn_dtype_t dtype, int B, int Hq, int Hkv, int N, int D,
+                                      int dtype, int B, int Hq, int Hkv, int N, int D,
                                       int causal, const float* lambda, float* out, void* stream);
 
 /*
@@ -131,10 +135,11 @@ diffattn_status_t diffattn_prefill_v2(const void* q, const void* k, const void* 
  * Layouts as for diffattn_prefill: q, k [B][H][N][ld] with d columns, v with
  * dv columns, out fp32 [B][H][N][dv].  causal != 0: query n sees keys 0..n.
  * Supported: BF16 with (d, dv) in {(64,128), (64,64)}; FP32 and other
- * shapes return UNSUPPORTED.  Other errors as for diffattn_prefill.
+ * shapes return UNSUPPORTED, as do token strides above 2^24 - 1 elements.
+ * Other errors as for diffattn_prefill.
  */
 diffattn_status_t diffattn_attention(const void* q, const void* k, const void* v, int64_t ldq,
-                                     int64_t ldk, int64_t ldv, diffattn_dtype_t dtype, int B,
+                                     int64_t ldk, int64_t ldv, int dtype, int B,
                                      int H, int N, int d, int dv, int causal, float* out,
                                      void* stream);
 
@@ -216,8 +221,9 @@ diffattn_status_t diffattn_decode_v1(const void* q, const void* k_cache, const v
                                      float norm_scale, const float* norm_weight, void* workspace,
                                      size_t workspace_bytes, float* out, void* stream);
 
-/* Static text for a status code. */
-const char* diffattn_status_string(diffattn_status_t status);
+/* Static text for a status code (a diffattn_status_t value; any other int
+ * gives "unknown status"). */
+const char* diffattn_status_string(int status);
 
 /* Detail of the last error reported on the calling thread ("" if none). */
 const char* diffattn_last_error(void);

@@ -215,3 +215,111 @@ def test_no_oracle_in_product_path():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liboracle" not in text, f
+
+
+# The bf16 kernels form copy offsets, tile strides and buffer extents of up to
+# 64 rows in 32-bit byte arithmetic: token strides from 2^24 elements on are
+# refused before anything is launched; 2^24 - 8 passes this check (and then
+# fails the device-pointer check on the fake address).
+BIG_LD = 1 << 24
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ldq=BIG_LD), UNSUPPORTED), (dict(ldk=BIG_LD), UNSUPPORTED),
+    (dict(ldv=BIG_LD), UNSUPPORTED), (dict(ldk=1 << 40), UNSUPPORTED),
+    (dict(ldq=BIG_LD - 8, ldk=BIG_LD - 8, ldv=BIG_LD - 8), INVALID),
+    (dict(dtype=0, ldq=BIG_LD, ldk=BIG_LD, ldv=BIG_LD), INVALID),   # fp32 path: 64-bit offsets
+])
+def test_prefill_stride_limit(lib, kw, code):
+    assert _prefill(lib, **kw) == code
+    if code == UNSUPPORTED:
+        assert "strides" in lib.diffattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ldq=BIG_LD), UNSUPPORTED), (dict(ldv=BIG_LD), UNSUPPORTED),
+    (dict(ldq=BIG_LD - 8, ldk=BIG_LD - 8, ldv=BIG_LD - 8), INVALID),
+])
+def test_attention_stride_limit(lib, kw, code):
+    assert _attention(lib, **kw) == code
+
+
+# The Python binding checks shapes, dtypes and devices before it calls the
+# library (CPU tensors: a call that passes these checks is then refused by the
+# library's device-pointer check, as DiffAttnError).
+def _decode_args(B=2, Hq=8, Hkv=2, D=128, L=64):
+    import torch
+    bf = torch.bfloat16
+    return dict(q=torch.zeros(B, Hq, D, dtype=bf), k_cache=torch.zeros(B, Hkv, L, D, dtype=bf),
+                v_cache=torch.zeros(B, Hkv, L, D, dtype=bf),
+                seq_lens=torch.full((B,), L, dtype=torch.int32),
+                lam=torch.zeros(Hq // 2, dtype=torch.float32))
+
+
+def _call_decode(a):
+    return api.diffattn_decode(a["q"], a["k_cache"], a["v_cache"], a["seq_lens"], a["lam"],
+                               workspace=a.get("workspace"), out=a.get("out"), stream=0)
+
+
+def test_binding_decode_accepts_consistent_tensors(lib):
+    with pytest.raises(api.DiffAttnError):
+        _call_decode(_decode_args())
+
+
+@pytest.mark.parametrize("change", [
+    "q_fp32", "k_fp32", "v_fp32", "v_short", "v_narrow", "lens_short", "lens_int64", "lam_short",
+    "lam_fp64", "k_batch", "out_shape",
+])
+def test_binding_decode_rejects(lib, change):
+    import torch
+    a = _decode_args()
+    if change == "q_fp32":
+        a["q"] = a["q"].float()
+    elif change == "k_fp32":
+        a["k_cache"] = a["k_cache"].float()
+    elif change == "v_fp32":
+        a["v_cache"] = a["v_cache"].float()
+    elif change == "v_short":
+        a["v_cache"] = a["v_cache"][:, :, :32].contiguous()
+    elif change == "v_narrow":
+        a["v_cache"] = a["v_cache"][..., :64].contiguous()
+    elif change == "lens_short":
+        a["seq_lens"] = a["seq_lens"][:1]
+    elif change == "lens_int64":
+        a["seq_lens"] = a["seq_lens"].long()
+    elif change == "lam_short":
+        a["lam"] = a["lam"][:3]
+    elif change == "lam_fp64":
+        a["lam"] = a["lam"].double()
+    elif change == "k_batch":
+        a["k_cache"] = torch.zeros(3, 2, 64, 128, dtype=torch.bfloat16)
+        a["v_cache"] = torch.zeros(3, 2, 64, 128, dtype=torch.bfloat16)
+    elif change == "out_shape":
+        a["out"] = torch.zeros(2, 8, 128)
+    with pytest.raises(ValueError):
+        _call_decode(a)
+
+
+@pytest.mark.parametrize("change", ["lam_short", "lam_bf16", "out_dtype", "k_shape"])
+def test_binding_prefill_rejects(lib, change):
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(1, 2, 16, 128, dtype=bf)
+    k = torch.zeros(1, 2, 16, 128, dtype=bf)
+    v = torch.zeros(1, 2, 16, 128, dtype=bf)
+    lam = torch.zeros(2)
+    out = None
+    if change == "lam_short":
+        lam = lam[:1]
+    elif change == "lam_bf16":
+        lam = lam.to(bf)
+    elif change == "out_dtype":
+        out = torch.zeros(1, 2, 16, 128, dtype=bf)
+    elif change == "k_shape":
+        k = torch.zeros(1, 2, 8, 128, dtype=bf)
+    with pytest.raises(ValueError):
+        api.diffattn_prefill_packed(q, k, v, lam, out=out, stream=0)
+    if change == "lam_short":   # the consistent call reaches the library
+        with pytest.raises(api.DiffAttnError):
+            api.diffattn_prefill_packed(q, torch.zeros(1, 2, 16, 128, dtype=bf), v, torch.zeros(2),
+                                        stream=0)
