@@ -54,16 +54,16 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int DEC_D = 128;             // head width
+constexpr int DEC_D = DECODE_D;        // head width
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
 constexpr int DEC_TILE = 32;           // keys per wave iteration
 constexpr int DEC_STEP = DEC_TILE * DEC_WAVES;   // keys per loop step of a workgroup
-constexpr int DEC_RANGE_MIN = 4096;    // shortest key range per workgroup
+constexpr int DEC_RANGE_MIN = DECODE_RANGE_MIN;   // shortest key range per workgroup
 constexpr int DEC_GROUP_MAX = 16;      // query heads per KV head that fit the MFMA columns
 constexpr int DEC_VROWB = DEC_D * 2;            // bytes per cached V row
 constexpr int DEC_VBYTES = DEC_TILE * DEC_VROWB; // one V tile, token-major (8 KB)
-constexpr int DEC_STATE = DEC_D + 2;            // floats per partial state: O[D], m*c, l
+constexpr int DEC_STATE = DECODE_STATE;         // floats per partial state: O[D], m*c, l
 constexpr float DEC_TAU = 8.0f;
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -103,8 +103,10 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return (unsigned)(size_t)((__attribute__((address_space(3))) const unsigned char*)p);
 }
 // 16 bytes per lane from global memory into LDS at lds_base + 16*lane, with the
-// non-temporal hint.  The compiler does not track these loads; the kernel waits
-// for them through the waits it emits for later loads (loads complete in order).
+// non-temporal hint.  The compiler does not track these loads.  Inside the key
+// loop the kernel relies on the waits it emits for the key loads issued after
+// each tile's copies (loads complete in issue order); before the LDS is reused
+// for the merge it waits for every load explicitly.
 __device__ __forceinline__ void copy16_to_lds_nt(i32x4 rsrc, unsigned lds_base, int voff) {
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base)
                  : "memory");
@@ -303,8 +305,9 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
             for (int e = 0; e < 8; e += 2) {
                 f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(sv[e], c, -mc)),
                             __builtin_amdgcn_exp2f(fmaf(sv[e + 1], c, -mc))};
-                ls += pr[0] + pr[1];
                 bf16x2 pb = __builtin_convertvector(pr, bf16x2);
+                // The normaliser sums the same bf16 probabilities the product uses.
+                ls = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, ls, false);
                 pf[e] = pb[0];
                 pf[e + 1] = pb[1];
             }
@@ -321,6 +324,10 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
         // inside it; idle waves carry m = -inf, l = 0, O = 0 and merge as nothing.
         lsum += __shfl_xor(lsum, 16);
         lsum += __shfl_xor(lsum, 32);
+        // The merge buffer below overlays the V tiles, which the untracked
+        // LDS copies write: every copy of this wave has landed before the
+        // barrier, whatever waits the compiler placed for the key loads.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();   // every wave is done reading its V tiles
         if (col_ok) {
             if (grp == 0) {
@@ -444,22 +451,6 @@ decode_merge_kernel(const float* __restrict__ ws, const int* __restrict__ piece_
 }
 
 }  // namespace
-
-bool decode_supported(int D) { return D == DEC_D; }
-
-// Pieces per segment: a segment of L <= max_len keys meets at most
-// ceil(L / R) + 1 ranges of R >= DEC_RANGE_MIN keys.
-int decode_max_splits(int max_len) { return (max_len + DEC_RANGE_MIN - 1) / DEC_RANGE_MIN + 1; }
-
-// Partial states [B][Hq][max_splits][DEC_STATE], then one piece count per
-// (sequence, KV head) (at most Hq of them per sequence).
-static size_t decode_state_floats(int B, int Hq, int max_len) {
-    return (size_t)B * Hq * decode_max_splits(max_len) * DEC_STATE;
-}
-size_t decode_workspace_floats(int B, int Hq, int D, int max_len) {
-    (void)D;
-    return decode_state_floats(B, Hq, max_len) + (size_t)B * Hq;
-}
 
 // Workgroups (= key ranges) of the split kernel: two per CU (its register
 // use allows two per CU), never more than ranges of DEC_RANGE_MIN keys can be
