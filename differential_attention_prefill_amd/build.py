@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 
-SOURCES = ["api.cpp", "lambda.hip", "prefill_f32.hip", "prefill_pp.hip", "combine.hip", "decode.hip"]
+SOURCES = ["api.cpp", "shapes.cpp", "lambda.hip", "prefill_f32.hip", "prefill_pp.hip", "combine.hip",
+           "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

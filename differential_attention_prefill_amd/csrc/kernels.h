@@ -1,5 +1,7 @@
 // Internal launch interface between the C-ABI layer (api.cpp) and the HIP
-// kernels.  Not installed; the public interface is include/diffattn.h.
+// kernels.  Not installed; the public interface is include/diffattn.h.  The
+// shape predicates and workspace sizing are plain host code (shapes.cpp); the
+// launch_* functions live with their kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -72,8 +74,17 @@ hipError_t launch_combine(const float* o1, const float* o2, const float* lambda,
 bool prefill_f32_supported(int d, int dv);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
+// Decode geometry shared by the kernels and the host-side sizing (shapes.cpp).
+constexpr int DECODE_D = 128;            // head width the decode kernels are built for
+constexpr int DECODE_RANGE_MIN = 4096;   // shortest key range per split workgroup
+constexpr int DECODE_STATE = DECODE_D + 2;   // floats per partial state: O[D], m*c, l
+
 bool decode_supported(int D);
+// Pieces (partial states) one (sequence, KV head) segment can be cut into.
 int decode_max_splits(int max_len);
+// Floats of partial states [B][Hq][decode_max_splits][DECODE_STATE]; the
+// piece counts (one int32 per (sequence, query head) slot) follow them.
+size_t decode_state_floats(int B, int Hq, int max_len);
 size_t decode_workspace_floats(int B, int Hq, int D, int max_len);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -144,10 +144,6 @@ hipError_t launch_f32(const PrefillArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-bool prefill_f32_supported(int d, int dv) {
-    return (d == 32 || d == 64 || d == 128) && (dv == 64 || dv == 128);
-}
-
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
 #define DIFFATTN_F32_CASE(DD, VV) \
     if (a.d == DD && a.dv == VV) return launch_f32<DD, VV>(a, stream);

@@ -939,11 +939,6 @@ hipError_t launch_ps(const PrefillArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-bool prefill_bf16_supported(int d, int dv) {
-    return (d == 64 && dv == 128) || (d == 64 && dv == 64) || (d == 32 && dv == 64) ||
-           (d == 128 && dv == 128);
-}
-
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     if (a.d == 64 && a.dv == 128) return launch_pp<64, 128, 2>(a, stream);
     if (a.d == 64 && a.dv == 64) return launch_pp<64, 64, 2>(a, stream);
@@ -951,10 +946,6 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     if (a.d == 128 && a.dv == 128)
         return a.k1 == a.k2 ? launch_ps<128, 128, true>(a, stream) : launch_ps<128, 128, false>(a, stream);
     return hipErrorInvalidValue;
-}
-
-bool attention_pp_supported(int d, int dv) {
-    return (d == 64 && dv == 128) || (d == 64 && dv == 64);
 }
 
 hipError_t launch_attention_pp(const PrefillArgs& a, hipStream_t stream) {
