@@ -671,7 +671,7 @@ def test_decode_v1_workload_scaled():
 # Signal-to-noise read off the kernel with probe values
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("N", [1024, 4096])
+@pytest.mark.parametrize("N", [1024, 4096, 16384, 65536])
 def test_snr_probe_matches_oracle(N):
     from differential_attention_prefill_amd import snr
     # A score of 10 keeps the signal weight well inside (0, 1) at these lengths.
