@@ -422,6 +422,18 @@ def measure_extras(dev, reps):
     return extras
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first /proc/cpuinfo entry), for the record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(pcase, pin, dcase, din, plam, dlam, norm_scale, target_s):
     """The CPU oracle, as it stands, on a bounded sample of the same step:
     uniformly drawn prefill query rows, plus the decode of a few sequences."""
@@ -461,7 +473,7 @@ def cpu_baseline(pcase, pin, dcase, din, plam, dlam, norm_scale, target_s):
     f2 = float(din["seq_lens"][:nb].sum().item()) * (dcase.Hq // 2) * 6 * dcase.D
     value = (f0 + f1 + f2) / (t0 + t1 + t2) / 1e12
     return {"value": round(value, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(t0 + t1 + t2, 2),
+            "cpu_model": cpu_model(), "seconds": round(t0 + t1 + t2, 2),
             "sample": "%d uniformly drawn query rows of the %d prefill rows (all their visible "
                       "keys, with the norm epilogue) + the decode of the first %d sequences; "
                       "fp64 C oracle, %d threads" % (4 * threads + n, total_rows, nb, threads)}
