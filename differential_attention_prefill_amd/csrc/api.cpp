@@ -306,59 +306,116 @@ size_t diffattn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_le
     return diffattn::decode_workspace_floats(B, Hq, D, max_len) * sizeof(float);
 }
 
-diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void* v_cache,
-                                  const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
-                                  int max_len, const float* lambda, void* workspace,
-                                  size_t workspace_bytes, float* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Pure-argument checks shared by the V2 decode entry points (everything but
+// the workspace), in the order the contract lists them.
+diffattn_status_t check_decode_args(const char* fn, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* seq_lens, int B, int Hq,
+                                    int Hkv, int D, int max_len, const float* lambda,
+                                    const float* out) {
     if (!q || !k_cache || !v_cache || !seq_lens || !lambda || !out)
-        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: null pointer");
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_len < 1)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
-                    "diffattn_decode: B=%d Hq=%d Hkv=%d D=%d max_len=%d must be >= 1", B, Hq, Hkv,
-                    D, max_len);
+                    "%s: B=%d Hq=%d Hkv=%d D=%d max_len=%d must be >= 1", fn, B, Hq, Hkv, D,
+                    max_len);
     if (Hq % (2 * Hkv) != 0)
-        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
-                    "diffattn_decode: Hq=%d must be a multiple of 2*Hkv=%d", Hq, 2 * Hkv);
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: Hq=%d must be a multiple of 2*Hkv=%d", fn,
+                    Hq, 2 * Hkv);
     const void* ptrs[6] = {q, k_cache, v_cache, seq_lens, lambda, out};
     const char* names[6] = {"q", "k_cache", "v_cache", "seq_lens", "lambda", "out"};
     for (int i = 0; i < 3; ++i)   // vector-loaded tensors
         if (!aligned16(ptrs[i]))
-            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: %s not 16-byte aligned",
-                        names[i]);
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: %s not 16-byte aligned", fn, names[i]);
     for (int i = 3; i < 6; ++i)   // read or written as 4-byte scalars
         if ((reinterpret_cast<uintptr_t>(ptrs[i]) & 3u) != 0)
-            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: %s not 4-byte aligned",
-                        names[i]);
+            return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: %s not 4-byte aligned", fn, names[i]);
     if (!diffattn::decode_supported(D))
-        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_decode: head width D=%d not built", D);
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "%s: head width D=%d not built", fn, D);
     if (Hq / Hkv > 16)
-        return fail(DIFFATTN_ERR_UNSUPPORTED,
-                    "diffattn_decode: %d query heads per KV head (at most 16)", Hq / Hkv);
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most 16)", fn,
+                    Hq / Hkv);
     if ((int64_t)B * Hkv * max_len > ((int64_t)1 << 40))
-        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: cache too large");
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: cache too large", fn);
     if (max_len > (1 << 30))
-        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: max_len too large");
-    const size_t need = diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len);
-    if (!workspace || workspace_bytes < need)
-        return fail(DIFFATTN_ERR_WORKSPACE, "diffattn_decode: workspace needs %zu bytes, got %zu",
-                    need, workspace ? workspace_bytes : (size_t)0);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: workspace not 256-byte aligned");
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: max_len too large", fn);
+    return DIFFATTN_OK;
+}
+
+diffattn_status_t check_decode_devices(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* seq_lens, const float* lambda,
+                                       const float* out) {
+    const void* ptrs[6] = {q, k_cache, v_cache, seq_lens, lambda, out};
+    const char* names[6] = {"q", "k_cache", "v_cache", "seq_lens", "lambda", "out"};
     for (int i = 0; i < 6; ++i) {
         diffattn_status_t s = check_device(ptrs[i], names[i]);
         if (s != DIFFATTN_OK) return s;
     }
-    {
-        diffattn_status_t s = check_device(workspace, "workspace");
-        if (s != DIFFATTN_OK) return s;
-    }
+    return DIFFATTN_OK;
+}
+
+diffattn::DecodeArgs decode_args(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                 int max_len, const float* lambda, void* workspace, float* out) {
     diffattn::DecodeArgs a;
     a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.seq_lens = seq_lens;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.max_len = max_len;
     a.lambda = lambda;
     a.workspace = static_cast<float*>(workspace);
     a.out = out;
-    return hip_status(diffattn::launch_decode(a, (hipStream_t)stream), "diffattn_decode launch");
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                  int max_len, const float* lambda, void* workspace,
+                                  size_t workspace_bytes, float* out, void* stream) {
+    diffattn_status_t s = check_decode_args("diffattn_decode", q, k_cache, v_cache, seq_lens, B,
+                                            Hq, Hkv, D, max_len, lambda, out);
+    if (s != DIFFATTN_OK) return s;
+    const size_t need = diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len);
+    if (!workspace || workspace_bytes < need)
+        return fail(DIFFATTN_ERR_WORKSPACE, "diffattn_decode: workspace needs %zu bytes, got %zu",
+                    need, workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_decode: workspace not 256-byte aligned");
+    s = check_decode_devices(q, k_cache, v_cache, seq_lens, lambda, out);
+    if (s != DIFFATTN_OK) return s;
+    s = check_device(workspace, "workspace");
+    if (s != DIFFATTN_OK) return s;
+    return hip_status(diffattn::launch_decode(decode_args(q, k_cache, v_cache, seq_lens, B, Hq,
+                                                          Hkv, D, max_len, lambda, workspace, out),
+                                              (hipStream_t)stream),
+                      "diffattn_decode launch");
+}
+
+diffattn_status_t diffattn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                          int max_len, const float* lambda, float* out,
+                                          void* stream) {
+    diffattn_status_t s = check_decode_args("diffattn_decode_noalloc", q, k_cache, v_cache,
+                                            seq_lens, B, Hq, Hkv, D, max_len, lambda, out);
+    if (s != DIFFATTN_OK) return s;
+    const size_t need = diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len);
+    if (need > DIFFATTN_DECODE_SCRATCH_BYTES)
+        return fail(DIFFATTN_ERR_WORKSPACE,
+                    "diffattn_decode_noalloc: these sizes need %zu bytes of partial states, the "
+                    "fixed scratch holds %zu; use diffattn_decode with a workspace",
+                    need, (size_t)DIFFATTN_DECODE_SCRATCH_BYTES);
+    s = check_decode_devices(q, k_cache, v_cache, seq_lens, lambda, out);
+    if (s != DIFFATTN_OK) return s;
+    return hip_status(diffattn::launch_decode_noalloc(decode_args(q, k_cache, v_cache, seq_lens, B,
+                                                                  Hq, Hkv, D, max_len, lambda,
+                                                                  nullptr, out),
+                                                      (hipStream_t)stream),
+                      "diffattn_decode_noalloc launch");
 }
 
 size_t diffattn_decode_v1_workspace_bytes(int B, int H, int max_len) {

@@ -471,6 +471,46 @@ static int decode_split_grid(int B, int Hkv, int max_len) {
     return (int)(ranges < want ? ranges : want);
 }
 
+// Fixed decode workspace for callers that cannot allocate: one copy of this
+// array per device, held until the process ends, shared by every
+// allocation-free call on that device (so such calls must not overlap).  The
+// kernels keep nothing in it across calls: every piece count and partial
+// state the merge reads is written by the same call's split kernel, so it
+// needs no clearing.  In host code the name is only a stand-in for the
+// symbol: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[DECODE_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int SCRATCH_DEVICES = 64;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there (a repeated first lookup from two threads stores the same value).
+static hipError_t scratch_address(float** out) {
+    static std::atomic<float*> addr[SCRATCH_DEVICES];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_DEVICES) return hipErrorInvalidDevice;
+    float* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(reinterpret_cast<void**>(&p), HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+hipError_t launch_decode_noalloc(const DecodeArgs& args, hipStream_t stream) {
+    if (decode_workspace_floats(args.B, args.Hq, args.D, args.max_len) * sizeof(float) >
+        DECODE_SCRATCH_BYTES)
+        return hipErrorInvalidValue;
+    DecodeArgs a = args;
+    const hipError_t e = scratch_address(&a.workspace);
+    if (e != hipSuccess) return e;
+    return launch_decode(a, stream);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (a.D != DEC_D || a.Hq / a.Hkv > DEC_GROUP_MAX) return hipErrorInvalidValue;
     const int S = decode_max_splits(a.max_len);

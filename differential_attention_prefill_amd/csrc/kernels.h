@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "diffattn.h"
+
 namespace diffattn {
 
 // Where the rows of diff head (b, h) start, in elements: q1 and q2 at
@@ -87,5 +89,10 @@ int decode_max_splits(int max_len);
 size_t decode_state_floats(int B, int Hq, int max_len);
 size_t decode_workspace_floats(int B, int Hq, int D, int max_len);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// The same decode with its partial states in the library's fixed per-device
+// scratch array (a.workspace is ignored); the caller has checked that the
+// workspace size fits DECODE_SCRATCH_BYTES.
+constexpr size_t DECODE_SCRATCH_BYTES = DIFFATTN_DECODE_SCRATCH_BYTES;
+hipError_t launch_decode_noalloc(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace diffattn

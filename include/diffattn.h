@@ -188,6 +188,25 @@ diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void
                                   size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * diffattn_decode without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * and harnesses that forbid hipMalloc.  Arguments, layouts, results and
+ * errors are those of diffattn_decode, less the workspace.  The partial
+ * states go to a fixed array of DIFFATTN_DECODE_SCRATCH_BYTES inside the
+ * library: one per device, created with the library's code on that device
+ * and held until the process ends.  Sizes whose
+ * diffattn_decode_workspace_bytes(...) exceed it return WORKSPACE (nothing is
+ * launched).  Nothing is allocated by this call.  Every call on one device
+ * shares that device's array, so calls that overlap on one device (on other
+ * streams or from other threads) race and must be ordered by the caller.
+ */
+#define DIFFATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+diffattn_status_t diffattn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                          int max_len, const float* lambda, float* out,
+                                          void* stream);
+
+/*
  * Bytes of device workspace diffattn_decode_v1 needs (two partial softmax
  * states, one per map, per head and KV piece, and a piece count per head).
  * Returns 0 for invalid sizes.

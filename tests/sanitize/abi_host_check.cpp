@@ -149,6 +149,24 @@ static void decode_cases() {
     const diffattn::DecodeArgs& a = g_stub.decode;
     CHECK(a.B == B && a.Hq == Hq && a.Hkv == Hkv && a.D == D && a.max_len == L && a.qhalf == 0);
 
+    // Allocation-free variant: the same checks, the fixed scratch bounds the sizes.
+    auto noalloc = [&](int b, int ml) {
+        return diffattn_decode_noalloc(q, k, v, (const int32_t*)lens, b, Hq, Hkv, D, ml,
+                                       (const float*)lam, (float*)out, nullptr);
+    };
+    CHECK(noalloc(B, L) == OK);
+    CHECK(std::strcmp(g_stub.last, "decode_noalloc") == 0 && g_stub.decode.workspace == nullptr);
+    CHECK(diffattn_decode_workspace_bytes(B, Hq, Hkv, D, L) <= DIFFATTN_DECODE_SCRATCH_BYTES);
+    const int before2 = g_stub.launches;
+    CHECK(diffattn_decode_workspace_bytes(64, Hq, Hkv, D, 1 << 20) > DIFFATTN_DECODE_SCRATCH_BYTES);
+    expect_reject(noalloc(64, 1 << 20), WSP);
+    CHECK(std::strstr(diffattn_last_error(), "scratch") != nullptr);
+    expect_reject(diffattn_decode_noalloc(q, k, v, (const int32_t*)lens, B, 30, Hkv, D, L,
+                                          (const float*)lam, (float*)out, nullptr), INV);
+    expect_reject(diffattn_decode_noalloc(q, k, v, (const int32_t*)lens, B, Hq, Hkv, D, L,
+                                          (const float*)lam, (float*)host(0), nullptr), INV);
+    CHECK(g_stub.launches == before2);
+
     // V1 layout: two query columns per head over its own rows.
     const size_t need1 = diffattn_decode_v1_workspace_bytes(B, 16, L);
     CHECK(need1 == diffattn_decode_workspace_bytes(B, 32, 16, 128, L));

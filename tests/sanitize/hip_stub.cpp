@@ -58,5 +58,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t) {
     g_stub.decode = a;
     return record("decode");
 }
+hipError_t launch_decode_noalloc(const DecodeArgs& a, hipStream_t) {
+    g_stub.decode = a;
+    return record("decode_noalloc");
+}
 
 }  // namespace diffattn
