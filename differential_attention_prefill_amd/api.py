@@ -24,7 +24,8 @@ STATUS = {0: "DIFFATTN_OK", 1: "DIFFATTN_ERR_INVALID_ARGUMENT", 2: "DIFFATTN_ERR
 
 EXPORTS = ("diffattn_lambda_init", "diffattn_lambda", "diffattn_prefill", "diffattn_prefill_v2",
            "diffattn_attention", "diffattn_combine",
-           "diffattn_decode_workspace_bytes", "diffattn_decode", "diffattn_decode_noalloc",
+           "diffattn_decode_workspace_bytes", "diffattn_decode", "diffattn_attention_decode",
+           "diffattn_decode_noalloc",
            "diffattn_decode_v1_workspace_bytes",
            "diffattn_decode_v1", "diffattn_status_string",
            "diffattn_last_error")
@@ -65,6 +66,8 @@ def load_library():
     lib.diffattn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.diffattn_decode.restype = I
     lib.diffattn_decode.argtypes = [P, P, P, P, I, I, I, I, I, P, P, S, P, P]
+    lib.diffattn_attention_decode.restype = I
+    lib.diffattn_attention_decode.argtypes = [P, P, P, P, I, I, I, I, I, P, S, P, P]
     lib.diffattn_decode_noalloc.restype = I
     lib.diffattn_decode_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P]
     lib.diffattn_decode_v1_workspace_bytes.restype = S
@@ -325,6 +328,42 @@ def diffattn_decode(q, k_cache, v_cache, seq_lens, lam, *, workspace=None, out=N
                                D, max_len, _ptr(lam), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _ptr(out),
                                _stream(stream)))
+    return out
+
+
+def diffattn_attention_decode(q, k_cache, v_cache, seq_lens, *, workspace=None, out=None,
+                              stream=None) -> torch.Tensor:
+    """Plain single-map GQA attention decode (the baseline the V2 layout is
+    compared with); returns fp32 [B, Hq, D].
+
+    q: bf16 [B, Hq, D]; k_cache, v_cache: bf16 [B, Hkv, max_len, D]; seq_lens:
+    int32 [B].  Query head h attends over KV head h // (Hq // Hkv).
+    """
+    lib = load_library()
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be contiguous bf16" % name)
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and the caches [B, Hkv, max_len, D]")
+    B, Hq, D = q.shape
+    _, Hkv, max_len, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, Hkv, max_len, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [B, Hkv, max_len, D] for q [B, Hq, D]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of B = %d entries" % B)
+    need = diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [B, Hq, D]")
+    _same_device((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens"),
+                 (workspace, "workspace"), (out, "out"))
+    _check(lib.diffattn_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B,
+                                         Hq, Hkv, D, max_len, _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _ptr(out),
+                                         _stream(stream)))
     return out
 
 

@@ -312,25 +312,28 @@ namespace {
 
 // Pure-argument checks shared by the V2 decode entry points (everything but
 // the workspace), in the order the contract lists them.
+// `paired`: differential heads (query heads 2p, 2p+1 over one KV head, a
+// lambda per pair); otherwise plain single-map heads (no lambda).
 diffattn_status_t check_decode_args(const char* fn, const void* q, const void* k_cache,
                                     const void* v_cache, const int32_t* seq_lens, int B, int Hq,
                                     int Hkv, int D, int max_len, const float* lambda,
-                                    const float* out) {
-    if (!q || !k_cache || !v_cache || !seq_lens || !lambda || !out)
+                                    const float* out, bool paired = true) {
+    if (!q || !k_cache || !v_cache || !seq_lens || (paired && !lambda) || !out)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_len < 1)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
                     "%s: B=%d Hq=%d Hkv=%d D=%d max_len=%d must be >= 1", fn, B, Hq, Hkv, D,
                     max_len);
-    if (Hq % (2 * Hkv) != 0)
-        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: Hq=%d must be a multiple of 2*Hkv=%d", fn,
-                    Hq, 2 * Hkv);
-    const void* ptrs[6] = {q, k_cache, v_cache, seq_lens, lambda, out};
-    const char* names[6] = {"q", "k_cache", "v_cache", "seq_lens", "lambda", "out"};
+    const int group = paired ? 2 * Hkv : Hkv;
+    if (Hq % group != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: Hq=%d must be a multiple of %s=%d", fn,
+                    Hq, paired ? "2*Hkv" : "Hkv", group);
+    const void* ptrs[6] = {q, k_cache, v_cache, seq_lens, out, lambda};
+    const char* names[6] = {"q", "k_cache", "v_cache", "seq_lens", "out", "lambda"};
     for (int i = 0; i < 3; ++i)   // vector-loaded tensors
         if (!aligned16(ptrs[i]))
             return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: %s not 16-byte aligned", fn, names[i]);
-    for (int i = 3; i < 6; ++i)   // read or written as 4-byte scalars
+    for (int i = 3; i < (paired ? 6 : 5); ++i)   // read or written as 4-byte scalars
         if ((reinterpret_cast<uintptr_t>(ptrs[i]) & 3u) != 0)
             return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "%s: %s not 4-byte aligned", fn, names[i]);
     if (!diffattn::decode_supported(D))
@@ -348,9 +351,9 @@ diffattn_status_t check_decode_args(const char* fn, const void* q, const void* k
 diffattn_status_t check_decode_devices(const void* q, const void* k_cache, const void* v_cache,
                                        const int32_t* seq_lens, const float* lambda,
                                        const float* out) {
-    const void* ptrs[6] = {q, k_cache, v_cache, seq_lens, lambda, out};
-    const char* names[6] = {"q", "k_cache", "v_cache", "seq_lens", "lambda", "out"};
-    for (int i = 0; i < 6; ++i) {
+    const void* ptrs[6] = {q, k_cache, v_cache, seq_lens, out, lambda};
+    const char* names[6] = {"q", "k_cache", "v_cache", "seq_lens", "out", "lambda"};
+    for (int i = 0; i < (lambda ? 6 : 5); ++i) {
         diffattn_status_t s = check_device(ptrs[i], names[i]);
         if (s != DIFFATTN_OK) return s;
     }
@@ -394,6 +397,32 @@ diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void
                                                           Hkv, D, max_len, lambda, workspace, out),
                                               (hipStream_t)stream),
                       "diffattn_decode launch");
+}
+
+diffattn_status_t diffattn_attention_decode(const void* q, const void* k_cache,
+                                            const void* v_cache, const int32_t* seq_lens, int B,
+                                            int Hq, int Hkv, int D, int max_len, void* workspace,
+                                            size_t workspace_bytes, float* out, void* stream) {
+    diffattn_status_t s = check_decode_args("diffattn_attention_decode", q, k_cache, v_cache,
+                                            seq_lens, B, Hq, Hkv, D, max_len, nullptr, out, false);
+    if (s != DIFFATTN_OK) return s;
+    const size_t need = diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len);
+    if (!workspace || workspace_bytes < need)
+        return fail(DIFFATTN_ERR_WORKSPACE,
+                    "diffattn_attention_decode: workspace needs %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                    "diffattn_attention_decode: workspace not 256-byte aligned");
+    s = check_decode_devices(q, k_cache, v_cache, seq_lens, nullptr, out);
+    if (s != DIFFATTN_OK) return s;
+    s = check_device(workspace, "workspace");
+    if (s != DIFFATTN_OK) return s;
+    diffattn::DecodeArgs a = decode_args(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, max_len,
+                                         nullptr, workspace, out);
+    a.single = 1;
+    return hip_status(diffattn::launch_decode(a, (hipStream_t)stream),
+                      "diffattn_attention_decode launch");
 }
 
 diffattn_status_t diffattn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,

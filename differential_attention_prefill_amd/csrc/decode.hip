@@ -384,7 +384,9 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
 // 256 threads: thread (m, ch) owns channel ch of head 2p+m.  The split maxima
 // are reduced once through LDS; each thread then sums its channel over the
 // splits with independent loads (unrolled), so the kernel is not a chain of
-// dependent global reads.
+// dependent global reads.  With `single` the two heads are independent
+// single-map heads (plain attention): each is normalised and written to
+// out [B][Hq][D], with no pairing, lambda or norm.
 constexpr int MERGE_THREADS = 2 * DEC_D;
 constexpr int MERGE_LDS_SPLITS = 1024;   // splits whose weights are cached in LDS
 
@@ -393,7 +395,7 @@ decode_merge_kernel(const float* __restrict__ ws, const int* __restrict__ piece_
                     const int32_t* __restrict__ seq_lens, int Hq, int Hkv, int max_len,
                     int max_splits, const float* __restrict__ lambda,
                     float* __restrict__ out, int rmsnorm, float eps, float norm_scale,
-                    const float* __restrict__ norm_weight) {
+                    const float* __restrict__ norm_weight, int single) {
     const int p = blockIdx.x;
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
@@ -401,17 +403,20 @@ decode_merge_kernel(const float* __restrict__ ws, const int* __restrict__ piece_
     const int ch = tid % DEC_D;
     const int P = Hq / 2;
     const int L = seq_lens[b];
-    float* o = out + ((int64_t)b * P + p) * DEC_D;
+    const int head = 2 * p + m;
+    const bool head_ok = head < Hq;   // an odd single-map head count leaves one idle
+    float* o = single ? out + ((int64_t)b * Hq + head) * DEC_D : out + ((int64_t)b * P + p) * DEC_D;
     if (L < 1 || L > max_len) {       // block-uniform
-        if (tid < DEC_D) o[tid] = 0.f;
+        if (single ? head_ok : tid < DEC_D) o[ch] = 0.f;
         return;
     }
     __shared__ float w_lds[2][MERGE_LDS_SPLITS];
     __shared__ float red[2][MERGE_THREADS / 64];
     __shared__ float res[DEC_D];
-    // Pieces of segment (b, g), written by the split kernel.
-    const int nsplit = min(piece_count[b * Hkv + (2 * p) / (Hq / Hkv)], max_splits);
-    const float* st = ws + ((int64_t)b * Hq + 2 * p + m) * max_splits * DEC_STATE;
+    // Pieces of segment (b, g) of this thread's head, written by the split
+    // kernel (both heads of a pair share g).
+    const int nsplit = head_ok ? min(piece_count[b * Hkv + head / (Hq / Hkv)], max_splits) : 0;
+    const float* st = ws + ((int64_t)b * Hq + (head_ok ? head : 0)) * max_splits * DEC_STATE;
 
     // Maximum of the split maxima of this thread's head (both heads at once:
     // threads 0..127 scan head 0, 128..255 head 1).
@@ -434,6 +439,10 @@ decode_merge_kernel(const float* __restrict__ ws, const int* __restrict__ piece_
         l = fmaf(st[(int64_t)s * DEC_STATE + DEC_D + 1], f, l);
     }
     const float r = acc / l;
+    if (single) {                     // block-uniform
+        if (head_ok) o[ch] = r;
+        return;
+    }
     if (m == 1) res[ch] = r;
     __syncthreads();
     const float y = r - lambda[p] * res[ch];     // meaningful for m == 0
@@ -523,9 +532,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
                            a.seq_lens, a.B, a.Hq, a.Hkv, a.max_len, S, a.workspace, counts, a.qhalf, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq / 2, a.B), dim3(MERGE_THREADS), 0, stream,
+    hipLaunchKernelGGL(decode_merge_kernel, dim3((a.Hq + 1) / 2, a.B), dim3(MERGE_THREADS), 0, stream,
                        a.workspace, counts, a.seq_lens, a.Hq, a.Hkv, a.max_len, S, a.lambda, a.out, a.rmsnorm,
-                       a.eps, a.norm_scale, a.norm_weight);
+                       a.eps, a.norm_scale, a.norm_weight, a.single);
     return hipGetLastError();
 }
 

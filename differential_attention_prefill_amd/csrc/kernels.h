@@ -56,6 +56,9 @@ struct DecodeArgs {
     int rmsnorm = 0;
     float eps = 0.f, norm_scale = 1.f;
     const float* norm_weight = nullptr;   // [D] or null
+    // Plain single-map attention when single != 0: every query head is its
+    // own softmax over its KV head's rows, out [B][Hq][D], lambda unused.
+    int single = 0;
 };
 
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,

@@ -188,6 +188,31 @@ diffattn_status_t diffattn_decode(const void* q, const void* k_cache, const void
                                   size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * Plain single-map softmax attention decode over the same GQA cache layout:
+ * every query head h is its own softmax over KV head h / (Hq/Hkv),
+ *     out[b,h] = softmax(q[b,h] K^T / sqrt(D)) V.
+ * It is the baseline decode that page "差分注意力" compares the V2 layout
+ * with ("V1 到 V2 的 diff", part 三 and part 五 exercise 3: doubling the
+ * query heads over the same KV heads keeps decode at the baseline's speed);
+ * a baseline model with half the query heads runs this over the cache a V2
+ * model reads.
+ *   q        : device bf16 [B][Hq][D]
+ *   k_cache,
+ *   v_cache  : device bf16 [B][Hkv][max_len][D]; positions 0..L_b-1 are read
+ *   seq_lens : device int32 [B]
+ *   out      : device fp32 [B][Hq][D]
+ * Hq must be a multiple of Hkv (at most 16 query heads per KV head).
+ * workspace: at least diffattn_decode_workspace_bytes(B, Hq, Hkv, D, max_len)
+ * bytes, 256-byte aligned, caller-owned.  Supported: D = 128.  A sequence
+ * whose device-side length is outside [1, max_len] yields zeros.  Errors as
+ * for diffattn_decode.
+ */
+diffattn_status_t diffattn_attention_decode(const void* q, const void* k_cache,
+                                            const void* v_cache, const int32_t* seq_lens, int B,
+                                            int Hq, int Hkv, int D, int max_len, void* workspace,
+                                            size_t workspace_bytes, float* out, void* stream);
+
+/*
  * diffattn_decode without a caller workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * and harnesses that forbid hipMalloc.  Arguments, layouts, results and

@@ -149,6 +149,21 @@ static void decode_cases() {
     const diffattn::DecodeArgs& a = g_stub.decode;
     CHECK(a.B == B && a.Hq == Hq && a.Hkv == Hkv && a.D == D && a.max_len == L && a.qhalf == 0);
 
+    // Plain single-map decode: Hq a multiple of Hkv, no lambda.
+    auto plain = [&](int hq, int hkv, size_t bytes) {
+        return diffattn_attention_decode(q, k, v, (const int32_t*)lens, B, hq, hkv, D, L, ws, bytes,
+                                         (float*)out, nullptr);
+    };
+    const size_t need16 = diffattn_decode_workspace_bytes(B, 16, Hkv, D, L);
+    CHECK(plain(16, Hkv, need16) == OK);
+    CHECK(g_stub.decode.single == 1 && g_stub.decode.Hq == 16 && g_stub.decode.lambda == nullptr);
+    CHECK(plain(8, 8, diffattn_decode_workspace_bytes(B, 8, 8, D, L)) == OK);    // one head per KV head
+    const int before3 = g_stub.launches;
+    expect_reject(plain(12, Hkv, need16), INV);
+    expect_reject(plain(16, Hkv, need16 - 4), WSP);
+    expect_reject(plain(Hkv * 17, Hkv, 1u << 30), UNS);
+    CHECK(g_stub.launches == before3);
+
     // Allocation-free variant: the same checks, the fixed scratch bounds the sizes.
     auto noalloc = [&](int b, int ml) {
         return diffattn_decode_noalloc(q, k, v, (const int32_t*)lens, b, Hq, Hkv, D, ml,

@@ -126,6 +126,27 @@ def test_decode_validation(lib, kw, code):
     assert _decode(lib, **kw) == code
 
 
+def _attention_decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, B=2, Hq=8, Hkv=4, D=128, max_len=4096,
+             ws=FAKE, ws_bytes=1 << 30, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.diffattn_attention_decode(a["q"], a["k"], a["v"], a["lens"], a["B"], a["Hq"],
+                                         a["Hkv"], a["D"], a["max_len"], a["ws"], a["ws_bytes"],
+                                         a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(B=0), INVALID),
+    (dict(Hq=6), INVALID), (dict(Hkv=0), INVALID), (dict(v=FAKE + 8), INVALID),
+    (dict(out=FAKE + 2), INVALID), (dict(ws=FAKE + 64), INVALID),
+    (dict(D=64), UNSUPPORTED), (dict(Hq=68, Hkv=4), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+    (dict(Hq=4, Hkv=4), INVALID),   # one head per KV head is valid: refused on the fake pointers
+])
+def test_attention_decode_validation(lib, kw, code):
+    assert _attention_decode(lib, **kw) == code
+
+
 def _attention(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, ldq=128, ldk=128, ldv=128, dtype=1, B=1, H=2, N=16, d=64,
              dv=128, causal=1, out=FAKE, stream=None)

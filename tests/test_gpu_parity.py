@@ -595,6 +595,73 @@ def test_decode_v2_workload_full():
 
 
 # ---------------------------------------------------------------------------
+# Plain single-map GQA decode (the baseline the V2 layout is compared with)
+# ---------------------------------------------------------------------------
+
+def _plain_decode_oracle(q, k_cache, v_cache, lens):
+    """Plain attention of every query head through the oracle's decode: a
+    query tensor of 2*Hq heads whose even heads are the plain heads and odd
+    heads zero, lambda = 0 (the oracle's pair p over KV head
+    2p // (2Hq/Hkv) = p // (Hq/Hkv) then gives A1 V of head p)."""
+    B, Hq, D = q.shape
+    q2 = torch.zeros((B, 2 * Hq, D), dtype=q.dtype)
+    q2[:, 0::2] = q
+    return oracle.decode(q2, k_cache, v_cache, lens, np.zeros(Hq, np.float32))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens", [
+    (4, 16, 8, [4096, 20000, 1, 9001]), (3, 8, 8, [1, 700, 333]), (2, 6, 2, [5000, 100]),
+    (3, 3, 3, [257, 1, 4100]), (2, 16, 1, [12289, 8191]),
+])
+def test_attention_decode_single_map(B, Hq, Hkv, lens):
+    case = W.DecodeCase("plain_decode_hq%d_hkv%d" % (Hq, Hkv), B=B, Hq=Hq, Hkv=Hkv, D=128,
+                        Lmin=1, Lmax=max(lens), layer=1, seed=B * 100 + Hq)
+    say("plain decode B=%d Hq=%d Hkv=%d lens=%s" % (B, Hq, Hkv, lens))
+    inp = W.make_decode(case, device=DEV)
+    inp["seq_lens"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    for b, L in enumerate(lens):   # unused cache slots hold NaN: they must not be read
+        inp["k_cache"][b, :, L:] = float("nan")
+        inp["v_cache"][b, :, L:] = float("nan")
+    out = torch.full((B, Hq, 128), float("nan"), device=DEV)
+    api.diffattn_attention_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], out=out)
+    torch.cuda.synchronize()
+    ref = _plain_decode_oracle(inp["q"].cpu(), inp["k_cache"].cpu(), inp["v_cache"].cpu(),
+                               inp["seq_lens"].cpu())
+    compare(out.cpu().numpy(), ref, "bf16", case.name)
+
+
+def test_attention_decode_invalid_length_gives_zeros():
+    case = W.DecodeCase("plain_decode_badlen", B=3, Hq=8, Hkv=2, D=128, Lmin=10, Lmax=300,
+                        layer=1, seed=6)
+    say("plain decode with out-of-range device lengths")
+    inp = W.make_decode(case, device=DEV)
+    inp["seq_lens"] = torch.tensor([120, 0, 301], dtype=torch.int32, device=DEV)
+    out = torch.full((3, 8, 128), float("nan"), device=DEV)
+    api.diffattn_attention_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[1:]).item() == 0
+    ref = _plain_decode_oracle(inp["q"][:1].cpu(), inp["k_cache"][:1].cpu(), inp["v_cache"][:1].cpu(),
+                               np.array([120], np.int32))
+    compare(out[:1].cpu().numpy(), ref, "bf16", "plain decode valid row")
+
+
+def test_v2_decode_equals_two_plain_decodes_combined():
+    # The differential decode of pair p is the plain decode of query head 2p
+    # minus lambda_p times that of head 2p+1 over the same KV head: both run
+    # the same split kernel, so the pieces are identical and only the final
+    # fp32 combination can differ.
+    case = W.scaled_decode(W.V2_DECODE, B=6, Lmin=1000, Lmax=30000, seed=81)
+    say("v2 decode against two plain decodes combined, %s B=%d" % (case.name, case.B))
+    inp = W.make_decode(case, device=DEV)
+    lam = gpu_lambda(inp, case.layer)
+    v2 = api.diffattn_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam)
+    plain = api.diffattn_attention_decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"])
+    torch.cuda.synchronize()
+    combined = plain[:, 0::2] - lam.view(1, -1, 1) * plain[:, 1::2]
+    assert (v2 - combined).abs().max().item() <= 1e-6
+
+
+# ---------------------------------------------------------------------------
 # V1-layout decode: half-width maps, value cache read once, RMS norm
 # ---------------------------------------------------------------------------
 
