@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the layouts measured beside the step (V2 prefill, ...)")
+    ap.add_argument("--only-extras", default="",
+                    help="comma-separated subset of the extras to run (%s)" % ", ".join(EXTRAS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -238,7 +240,11 @@ def main():
     if not args.no_extras:
         del pin, din, q1, q2, k1, k2, v, pout, dout, ws
         torch.cuda.empty_cache()
-        result["extras"] = measure_extras(dev, max(3, args.steps))
+        only = [x for x in args.only_extras.split(",") if x]
+        for x in only:
+            if x not in EXTRAS:
+                raise SystemExit("unknown extra %r (choose from %s)" % (x, ", ".join(EXTRAS)))
+        result["extras"] = measure_extras(dev, max(3, args.steps), set(only or EXTRAS))
         pin = din = None
 
     if not args.no_cpu_baseline:
@@ -265,14 +271,34 @@ def _time_launches(fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def measure_extras(dev, reps):
+EXTRAS = ("prefill_workloads", "v2_prefill", "unfused_vs_fused", "v1_decode", "baseline_decode",
+          "snr_sweep")
+
+
+def measure_extras(dev, reps, which=frozenset(EXTRAS)):
     """Layouts measured beside the step, each on its own synthetic workload."""
+    extras = {}
+    if "prefill_workloads" in which:
+        extras["prefill_workloads"] = _extra_prefill_workloads(dev, reps)
+    if "v2_prefill" in which:
+        extras["v2_prefill"] = _extra_v2_prefill(dev, reps)
+    if "unfused_vs_fused" in which:
+        extras["unfused_vs_fused"] = _extra_unfused(dev, reps)
+    if "v1_decode" in which:
+        extras["v1_decode"] = _extra_v1_decode(dev, reps)
+    if "baseline_decode" in which:
+        extras["baseline_decode"] = _extra_baseline_decode(dev, reps)
+    if "snr_sweep" in which:
+        extras.update(_extra_snr(dev))
+    return extras
+
+
+def _extra_prefill_workloads(dev, reps):
     import torch
 
     from differential_attention_prefill_amd import api
     from differential_attention_prefill_amd import workloads as W
 
-    extras = {}
     # The other prefill workloads the operator is specified on, each timed on
     # its own: the tiny fp32 case (vector-ALU path, launch-bound: no roofline
     # claim), the V1 norm workload at N = 2048 and the 32k needle workload
@@ -307,7 +333,14 @@ def measure_extras(dev, reps):
         per_cfg[c.name] = rec
         del inp, out
         torch.cuda.empty_cache()
-    extras["prefill_workloads"] = per_cfg
+    return per_cfg
+
+
+def _extra_v2_prefill(dev, reps):
+    import torch
+
+    from differential_attention_prefill_amd import api
+    from differential_attention_prefill_amd import workloads as W
 
     # V2 prefill: doubled query heads over shared K/V heads, D = 128 for both maps.
     c = W.V2_PREFILL_32K
@@ -319,16 +352,27 @@ def measure_extras(dev, reps):
     ms = _time_launches(lambda: api.diffattn_prefill_v2(inp["q"], inp["k"], inp["v"], lam,
                                                         causal=c.causal, out=out), reps)
     f = float(c.pairs()) * (4 * c.D + 2 * c.D)
-    extras["v2_prefill"] = {"workload": c.name, "avg_launch_ms": round(ms, 4),
-                            "algorithmic_flops_per_launch": f,
-                            "achieved_tflops": round(f / (ms * 1e-3) / 1e12, 2),
-                            "frac_of_bf16_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    rec = {"workload": c.name, "avg_launch_ms": round(ms, 4),
+           "algorithmic_flops_per_launch": f,
+           "achieved_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+           "frac_of_bf16_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     del inp, out
     torch.cuda.empty_cache()
+    return rec
+
+
+def _extra_unfused(dev, reps):
+    import torch
+
+    from differential_attention_prefill_amd import api
+    from differential_attention_prefill_amd import workloads as W
 
     # Unfused two-pass path on the step's prefill workload: single-map
     # attention for each map (V read twice, two fp32 intermediates), then the
-    # combine pass; beside the fused kernel on the same inputs.
+    # combine pass; beside the fused kernel on the same inputs.  The device
+    # memory each path needs beyond its inputs is read from torch's allocator
+    # (the library allocates nothing): the fused call holds only its output,
+    # the same as a plain attention of this width would.
     c = W.MULTI_NEEDLE_64K
     print("# extras: unfused vs fused, %s" % c.name, file=sys.stderr, flush=True)
     inp = W.make_prefill(c, device=dev)
@@ -338,12 +382,31 @@ def measure_extras(dev, reps):
                               layer=c.layer)
     scale = 1.0 - api.diffattn_lambda_init(c.layer)
     shape = (c.B, c.H, c.N, c.dv)
+    torch.cuda.synchronize()
+    inputs_bytes = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+
+    def fused_call(out):
+        api.diffattn_prefill(q[..., :d], q[..., d:], k[..., :d], k[..., d:], v, lam, causal=True,
+                             rmsnorm=c.rmsnorm, eps=c.eps, norm_scale=scale, out=out)
+
+    out = torch.empty(shape, dtype=torch.float32, device=dev)
+    fused_call(out)
+    torch.cuda.synchronize()
+    fused_peak = torch.cuda.max_memory_allocated() - inputs_bytes
+    del out
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
     o1 = torch.empty(shape, dtype=torch.float32, device=dev)
     o2 = torch.empty(shape, dtype=torch.float32, device=dev)
     out = torch.empty(shape, dtype=torch.float32, device=dev)
-    fused_ms = _time_launches(lambda: api.diffattn_prefill(
-        q[..., :d], q[..., d:], k[..., :d], k[..., d:], v, lam, causal=True, rmsnorm=c.rmsnorm,
-        eps=c.eps, norm_scale=scale, out=out), reps)
+    api.diffattn_attention(q[..., :d], k[..., :d], v, out=o1)
+    api.diffattn_attention(q[..., d:], k[..., d:], v, out=o2)
+    api.diffattn_combine(o1, o2, lam, rmsnorm=c.rmsnorm, eps=c.eps, norm_scale=scale, out=out)
+    torch.cuda.synchronize()
+    unfused_peak = torch.cuda.max_memory_allocated() - inputs_bytes
+
+    fused_ms = _time_launches(lambda: fused_call(out), reps)
     att_ms = _time_launches(lambda: (api.diffattn_attention(q[..., :d], k[..., :d], v, out=o1),
                                      api.diffattn_attention(q[..., d:], k[..., d:], v, out=o2)),
                             reps)
@@ -353,17 +416,28 @@ def measure_extras(dev, reps):
     in_bytes = rows * (2 * (2 * d) * 2 + c.dv * 2)          # q and k (both halves), v
     out_bytes = rows * c.dv * 4
     inter = 2 * rows * c.dv * 4                              # o1 and o2
-    extras["unfused_vs_fused"] = {
+    rec = {
         "workload": c.name, "fused_ms": round(fused_ms, 4),
         "unfused_ms": round(att_ms + cmb_ms, 4), "unfused_attention_ms": round(att_ms, 4),
         "unfused_combine_ms": round(cmb_ms, 4),
         "fused_speedup": round((att_ms + cmb_ms) / fused_ms, 3),
         "fused_hbm_bytes_model": in_bytes + out_bytes,
         "unfused_hbm_bytes_model": in_bytes + rows * c.dv * 2 + 2 * inter + out_bytes,
-        "unfused_extra_device_bytes": inter,
+        "inputs_device_bytes": int(inputs_bytes),
+        "fused_device_bytes_beyond_inputs": int(fused_peak),
+        "unfused_device_bytes_beyond_inputs": int(unfused_peak),
+        "fused_footprint_vs_unfused": round((inputs_bytes + fused_peak) / (inputs_bytes + unfused_peak), 4),
     }
     del inp, q, k, v, o1, o2, out
     torch.cuda.empty_cache()
+    return rec
+
+
+def _extra_v1_decode(dev, reps):
+    import torch
+
+    from differential_attention_prefill_amd import api
+    from differential_attention_prefill_amd import workloads as W
 
     # V1-layout decode: half-width maps over per-head K1|K2 and V caches, RMS norm.
     c = W.V1_DECODE
@@ -381,13 +455,60 @@ def measure_extras(dev, reps):
     lens = inp["seq_lens"].cpu().tolist()
     nbytes = float(sum(int(x) for x in lens)) * c.H * (2 * c.d + c.dv) * 2 + \
         c.B * c.H * (2 * c.d * 2 + c.dv * 4) + c.H * 4 + c.B * 4
-    extras["v1_decode"] = {"workload": c.name, "avg_launch_ms": round(ms, 4),
-                           "algorithmic_bytes_per_launch": nbytes,
-                           "achieved_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                           "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    rec = {"workload": c.name, "avg_launch_ms": round(ms, 4),
+           "algorithmic_bytes_per_launch": nbytes,
+           "achieved_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     del inp, ws, out
     torch.cuda.empty_cache()
+    return rec
 
+
+def _extra_baseline_decode(dev, reps):
+    import torch
+
+    from differential_attention_prefill_amd import api
+    from differential_attention_prefill_amd import workloads as W
+
+    # The decode the V2 layout is compared with: a baseline model whose heads
+    # are single softmax maps, with half the query heads (16) over the same
+    # 8 KV heads and the same cache, timed beside the V2 differential decode
+    # (32 query heads = 16 pairs) on that cache.
+    c = W.V2_DECODE
+    print("# extras: baseline decode vs V2 decode, %s" % c.name, file=sys.stderr, flush=True)
+    inp = W.make_decode(c, device=dev)
+    lam = api.diffattn_lambda(*(inp[x].contiguous() for x in ("lq1", "lk1", "lq2", "lk2")),
+                              layer=c.layer)
+    hb = c.Hq // 2
+    qb = inp["q"][:, 0::2].contiguous()          # one query per baseline head
+    ws = torch.empty(api.diffattn_decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.D, c.Lmax),
+                     dtype=torch.uint8, device=dev)
+    out2 = torch.empty((c.B, c.Hq // 2, c.D), dtype=torch.float32, device=dev)
+    outb = torch.empty((c.B, hb, c.D), dtype=torch.float32, device=dev)
+    v2_ms = _time_launches(lambda: api.diffattn_decode(inp["q"], inp["k_cache"], inp["v_cache"],
+                                                       inp["seq_lens"], lam, workspace=ws, out=out2),
+                           max(reps, 20))
+    base_ms = _time_launches(lambda: api.diffattn_attention_decode(
+        qb, inp["k_cache"], inp["v_cache"], inp["seq_lens"], workspace=ws, out=outb), max(reps, 20))
+    lens = inp["seq_lens"].cpu().tolist()
+    kv = float(sum(int(x) for x in lens)) * c.Hkv * 2 * c.D * 2
+    rec = {"workload": c.name, "v2_query_heads": c.Hq, "baseline_query_heads": hb,
+           "kv_heads": c.Hkv, "v2_ms": round(v2_ms, 4), "baseline_ms": round(base_ms, 4),
+           "v2_over_baseline": round(v2_ms / base_ms, 4), "kv_cache_bytes_read": kv,
+           "v2_gbps": round(kv / (v2_ms * 1e-3) / 1e9, 1),
+           "baseline_gbps": round(kv / (base_ms * 1e-3) / 1e9, 1)}
+    del inp, ws, out2, outb, qb
+    torch.cuda.empty_cache()
+    return rec
+
+
+def _extra_snr(dev):
+    import torch
+
+    from differential_attention_prefill_amd import api
+    from differential_attention_prefill_amd import workloads as W
+
+    extras = {}
     # Signal-to-noise of the last query towards a planted needle, plain vs
     # differential, as the context grows (kernel run with probe values).
     from differential_attention_prefill_amd import snr
