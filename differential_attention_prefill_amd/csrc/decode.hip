@@ -84,9 +84,11 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // V tiles reach LDS straight from global memory (buffer loads that write LDS:
 // no staging registers) and leave it through the gfx950 transpose load, which
 // hands each lane 4 consecutive keys of one channel.  Rows are stored with
-// their 32-byte channel slots XOR-swizzled by the row's low 3 bits, so the 4
-// rows one 16-lane group reads land in distinct banks.
-__device__ __forceinline__ int vslot_swz(int row) { return row & 7; }
+// their 32-byte channel slots XOR-swizzled so that the 4 rows one 16-lane
+// group reads (rows 8G + 0..3, or + 4..7) and the 4 rows of the neighbouring
+// group (8(G+1) + the same) take 8 distinct slots: the 32 lanes served
+// together touch every bank once.
+__device__ __forceinline__ int vslot_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
 
 // Raw buffer descriptor (gfx9-family layout): base, stride 0, byte extent;
 // loads at offsets >= `bytes` return zeros.
@@ -141,12 +143,16 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
                     int Hq, int Hkv, int max_len, int max_splits, float* __restrict__ ws,
                     int* __restrict__ piece_count, int qhalf, float c) {
     // Two V tiles per wave during the stream; reused as the wave-merge buffer.
+    // Each lane stores 16 bytes per block; head rows are padded to 132 floats
+    // (528 bytes), so the 16 heads of one store's 16 lanes start 4 banks apart
+    // and fill all 64 banks.
     __shared__ __attribute__((aligned(16))) unsigned char lds[DEC_WAVES * 2 * DEC_VBYTES];
     __shared__ float merge_m[DEC_WAVES][DEC_GROUP_MAX];
     __shared__ float merge_l[DEC_WAVES][DEC_GROUP_MAX];
-    static_assert(DEC_WAVES * DEC_GROUP_MAX * DEC_D * 4 <= DEC_WAVES * 2 * DEC_VBYTES,
+    constexpr int MROW = DEC_D + 4;
+    static_assert(DEC_WAVES * DEC_GROUP_MAX * MROW * 4 <= DEC_WAVES * 2 * DEC_VBYTES,
                   "merge buffer must fit in the V tiles");
-    float (*merge_o)[DEC_GROUP_MAX][DEC_D] = reinterpret_cast<float (*)[DEC_GROUP_MAX][DEC_D]>(lds);
+    float (*merge_o)[DEC_GROUP_MAX][MROW] = reinterpret_cast<float (*)[DEC_GROUP_MAX][MROW]>(lds);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -336,8 +342,7 @@ decode_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ kc,
             }
     #pragma unroll
             for (int blk = 0; blk < 8; ++blk)
-    #pragma unroll
-                for (int r = 0; r < 4; ++r) merge_o[wave][col][blk * 16 + grp * 4 + r] = acc[blk][r];
+                *reinterpret_cast<f32x4*>(&merge_o[wave][col][blk * 16 + grp * 4]) = acc[blk];
         }
         __syncthreads();
         // Merge the waves: thread = (head, channel).
