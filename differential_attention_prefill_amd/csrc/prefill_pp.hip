@@ -299,9 +299,6 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     };
     static_assert(C::CPW >= 1 && C::CPW <= 15, "copies per wave must fit the vmcnt field");
 
-    auto stage_of = [&](int j) -> const unsigned char* {
-        return smem + ((j >> 1) % PP_NSTAGE) * C::STAGE;
-    };
 
     // M(j), for j <= jmax: P.V of sub-tile j-1 (both maps share each V^T
     // fragment) and the scores of sub-tile j for both maps, as one software
@@ -316,19 +313,22 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // The derived LDS offsets are rematerialised per use (fresh) rather than
     // kept per lane.
     auto read_v = [&](const unsigned char* vs, int u, bf16x8 (&dst)[2]) {
+        // One lane address per unit; the four reads differ by constants.
+        const unsigned char* vu = vs + (u ? (vx ^ fresh(64 * u)) : vx);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
-            const unsigned char* vp = vs + (u ? (vx ^ fresh(64 * u)) : vx) + t2 * 16 * C::VROWB;
+            const unsigned char* vp = vu + t2 * 16 * C::VROWB;
             const bf16x4 lo = lds_read_tr(vp);
             const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
             dst[t2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    auto m_phase = [&](int j) {
+    // so_j, so_v: byte offsets of the stages holding sub-tiles j and j - 1.
+    auto m_phase = [&](int j, int so_j, int so_v) {
         if (j > jmax) return;
         const int jv = j > 0 ? j - 1 : 0;
-        const unsigned char* vs = stage_of(jv) + (jv & 1) * BN * C::VROWB;
-        const unsigned char* ks = stage_of(j) + (j & 1) * BN * C::KROWB;
+        const unsigned char* vs = smem + so_v + (jv & 1) * BN * C::VROWB;
+        const unsigned char* ks = smem + so_j + (j & 1) * BN * C::KROWB;
         constexpr int NU = C::VBLK + C::KSTEPS;
         bf16x8 vf[C::VBLK][2];
         bf16x8 kf[MAPS][C::KSTEPS];
@@ -337,10 +337,11 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
                 read_v(vs, u, vf[u < C::VBLK ? u : 0]);
             } else {
                 const int st = u - C::VBLK;
+                // One lane address for both maps' reads of this k-step.
+                const unsigned char* ku = ks + (st ? (kx ^ fresh(32 * st)) : kx);
 #pragma unroll
                 for (int m = 0; m < MAPS; ++m)
-                    kf[m][st] = __builtin_bit_cast(
-                        bf16x8, load16(ks + m * C::K2_OFF + (st ? (kx ^ fresh(32 * st)) : kx)));
+                    kf[m][st] = __builtin_bit_cast(bf16x8, load16(ku + m * C::K2_OFF));
             }
         };
 #pragma unroll
@@ -371,7 +372,7 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         }
         // Units 0 and 1 of M(j+1): the values of sub-tile j, visible now (its
         // keys were read above) and not overwritten before M(j+1).
-        const unsigned char* vsn = stage_of(j) + (j & 1) * BN * C::VROWB;
+        const unsigned char* vsn = smem + so_j + (j & 1) * BN * C::VROWB;
         read_v(vsn, 0, vnext[0]);
         read_v(vsn, 1, vnext[1]);
         PipeGroupsN<0, NU, C::VBLK, MAPS, true, 2>::run();
@@ -474,9 +475,12 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     if (grp) phase_barrier();   // group 1 starts one phase later
     // The wave in its matrix phase takes issue priority over the one in its
     // softmax phase on the same SIMD, so the matrix core is fed first.
+    // The stage ring advances every second sub-tile; its offsets are carried
+    // through the loop rather than recomputed modulo the stage count.
+    int so_j = 0, so_v = 0;
     for (int j = 0; j <= nsub; ++j) {
         __builtin_amdgcn_s_setprio(1);
-        m_phase(j);
+        m_phase(j, so_j, so_v);
         if (j & 1) {
             // Copy tile (j+3)/2, then wait for tile (j+1)/2 with only the
             // copies just issued still in flight.
@@ -489,6 +493,8 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         __builtin_amdgcn_s_setprio(0);
         v_phase(j);
         phase_barrier();
+        so_v = so_j;
+        if (j & 1) so_j = (so_j + C::STAGE == PP_NSTAGE * C::STAGE) ? 0 : so_j + C::STAGE;
     }
     __builtin_amdgcn_s_setprio(0);
     if (!grp) phase_barrier();  // matches group 1's extra barrier
@@ -725,28 +731,27 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             copy16_to_lds(r, st + (wave + PS_WAVES * bb) * 1024, coff[bb]);
         }
     };
-    auto stage_of = [&](int j) -> const unsigned char* {
-        return smem + ((j >> 1) % PP_NSTAGE) * C::STAGE;
-    };
 
     // M(j), j <= jmax: this map's P.V of sub-tile j-1 (4 V^T blocks) and its
     // scores of sub-tile j (8 key k-steps), one pipeline with the loads PS_PD
     // units ahead; at j = 0 the probabilities are zero, at j = jmax the scores
     // are dropped (as in the d <= 64 kernel).
     auto read_v = [&](const unsigned char* vs, int u, bf16x8 (&dst)[2]) {
+        const unsigned char* vu = vs + (u ? (vx ^ fresh(64 * u)) : vx);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
-            const unsigned char* vp = vs + (u ? (vx ^ fresh(64 * u)) : vx) + t2 * 16 * C::VROWB;
+            const unsigned char* vp = vu + t2 * 16 * C::VROWB;
             const bf16x4 lo = lds_read_tr(vp);
             const bf16x4 hi = lds_read_tr(vp + 4 * C::VROWB);
             dst[t2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    auto m_phase = [&](int j) {
+    // so_j, so_v: byte offsets of the stages holding sub-tiles j and j - 1.
+    auto m_phase = [&](int j, int so_j, int so_v) {
         if (j > jmax) return;
         const int jv = j > 0 ? j - 1 : 0;
-        const unsigned char* vs = stage_of(jv) + (jv & 1) * BN * C::VROWB;
-        const unsigned char* ks = stage_of(j) + (j & 1) * BN * C::KROWB;
+        const unsigned char* vs = smem + so_v + (jv & 1) * BN * C::VROWB;
+        const unsigned char* ks = smem + so_j + (j & 1) * BN * C::KROWB;
         constexpr int NU = C::VBLK + C::KSTEPS;
         bf16x8 vf[C::VBLK][2];
         bf16x8 kf[C::KSTEPS];
@@ -777,7 +782,7 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             if (u + PS_PD < NU) load_unit(u + PS_PD);
         }
         // The first units of M(j+1): the values of sub-tile j.
-        const unsigned char* vsn = stage_of(j) + (j & 1) * BN * C::VROWB;
+        const unsigned char* vsn = smem + so_j + (j & 1) * BN * C::VROWB;
 #pragma unroll
         for (int u = 0; u < PS_PD; ++u) read_v(vsn, u, vnext[u]);
         PipeGroupsN<0, NU, C::VBLK, 1, false, PS_PD>::run();
@@ -843,9 +848,10 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     for (int u = 0; u < PS_PD; ++u)  // M(0): values of sub-tile 0 (times zero probabilities)
         read_v(smem, u, vnext[u]);
     if (grp) phase_barrier();
+    int so_j = 0, so_v = 0;   // stage ring offsets, carried as in the d <= 64 kernel
     for (int j = 0; j <= nsub; ++j) {
         __builtin_amdgcn_s_setprio(1);
-        m_phase(j);
+        m_phase(j, so_j, so_v);
         if (j & 1) {
             // Copy tile (j+3)/2, then wait for tile (j+1)/2 with only the
             // copies just issued still in flight.
@@ -858,6 +864,8 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
         __builtin_amdgcn_s_setprio(0);
         v_phase(j);
         phase_barrier();
+        so_v = so_j;
+        if (j & 1) so_j = (so_j + C::STAGE == PP_NSTAGE * C::STAGE) ? 0 : so_j + C::STAGE;
     }
     __builtin_amdgcn_s_setprio(0);
     if (!grp) phase_barrier();
