@@ -373,6 +373,27 @@ def test_prefill_causality_and_determinism(d):
     assert not torch.equal(a[:, :, i + 1:], c[:, :, i + 1:])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_prefill_nonfinite_key_row_is_causal(d, bad):
+    # Causal masking replaces the scores of keys after a query before they are
+    # used, so a non-finite key row j leaves every output row i < j exactly as
+    # it was (page "差分注意力", part 二 Step 2: query i attends to keys 0..i).
+    # Rows at the start, inside and at the end of 32-key sub-tiles and of
+    # 256-row tiles.
+    B, H, N, dv = 1, 2, 600, 128
+    q, k, v = _rand_bf16((B, H, N, 2 * d), 16), _rand_bf16((B, H, N, 2 * d), 17), _rand_bf16((B, H, N, dv), 18)
+    lam = torch.tensor([0.3, 0.6], device=DEV)
+    clean = api.diffattn_prefill_packed(q, k, v, lam)
+    for j in (1, 31, 32, 170, 255, 256, 511, 599):
+        say("bf16 non-finite key row d=%d bad=%s j=%d" % (d, bad, j))
+        kb = k.clone()
+        kb[:, :, j] = bad
+        out = api.diffattn_prefill_packed(q, kb, v, lam)
+        assert torch.equal(out[:, :, :j], clean[:, :, :j]), j
+        torch.cuda.synchronize()
+
+
 def test_prefill_separate_tensors_match_packed():
     B, H, N, d, dv = 1, 2, 96, 64, 128
     say("bf16 separate Q1/Q2/K1/K2 tensors")
