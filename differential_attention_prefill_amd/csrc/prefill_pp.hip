@@ -18,20 +18,22 @@
 //  - Each 32-key sub-tile j is two phases per wave: M(j) issues the matrix
 //    products (P.V of sub-tile j-1 and the scores of sub-tile j, both maps,
 //    as one pipeline over operand units), V(j) runs both online softmaxes of sub-tile
-//    j on the vector ALU.  The waves form two groups, and the second runs one
-//    phase behind the first, with a workgroup barrier after every phase:
-//    while one group's matrix products occupy a SIMD's matrix core, the
-//    other group's softmax occupies its vector ALU.  Waves w and w+4 share a
-//    SIMD and take adjacent row blocks 2w and 2w+1, so they have the same
-//    causal extent and stay balanced.
+//    j on the vector ALU.  The waves form two groups that meet at one
+//    workgroup barrier per interval: interval j holds group 0's M(j) and
+//    V(j) and group 1's V(j-1) and M(j) (group 1 places its barrier between
+//    its M and V phases, group 0 after its V phase), so while one group's
+//    matrix products occupy a SIMD's matrix core, the other group's softmax
+//    occupies its vector ALU.  Waves w and w+4 share a SIMD and take
+//    adjacent row blocks 2w and 2w+1, so they have the same causal extent
+//    and stay balanced.
 //  - Keys and values stream through LDS in tiles of 64 keys, three stages
 //    deep, copied by buffer loads that write LDS directly.  Tile t is read
-//    by the M phases of steps 2t .. 2t+2.  Every wave copies the same number
-//    of 1 KB blocks of it, in one burst at the end of its M phase of step
-//    2t-3 (global phase 4t-6 or 4t-5), into the stage that tile t-3 left
-//    after phase 4t-7, and waits for it at the end of its M phase of step
-//    2t-1 with exactly the copies of tile t+1, issued just before, still in
-//    flight (copies complete in issue order); the barrier ending phase 4t-1
+//    by the M phases of steps 2t .. 2t+2 (intervals 2t .. 2t+2).  Every wave
+//    copies the same number of 1 KB blocks of it, in one burst at the end of
+//    its M phase of step 2t-3, into the stage that tile t-3 left in interval
+//    2t-4, and waits for it at the end of its M phase of step 2t-1 with
+//    exactly the copies of tile t+1, issued just before, still in flight
+//    (copies complete in issue order); the barrier ending interval 2t-1
 //    publishes the tile.  The softmax phase carries no copy work.
 //  - Scores are formed transposed, S^T = K . Q^T (v_mfma_f32_32x32x16_bf16):
 //    a lane holds 16 keys of ONE query, so each softmax row statistic is a
@@ -454,14 +456,14 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     };
 
     // ---- the schedule ------------------------------------------------------
-    // Global phase p: group 0 runs M(j) at p = 2j and V(j) at 2j+1, group 1
-    // runs M(j) at 2j+1 and V(j) at 2j+2.  Tile t (sub-tiles 2t, 2t+1) is read
-    // by M(2t) .. M(2t+2), phases 4t .. 4t+5.  M(2t-3) copies it into the
-    // stage tile t-3 left after phase 4t-7; M(2t-1) waits for it, and the
-    // barrier ending phase 4t-1 publishes it.  (tests/test_copy_schedule.py
-    // models both groups over every key extent up to 2560 and at 4k/32k/64k:
-    // each copy issued once into a free stage, complete and published before
-    // its first read, none in flight at the end.)
+    // Interval j ends with the workgroup's j-th loop barrier and holds both
+    // groups' M(j).  Tile t (sub-tiles 2t, 2t+1) is read by M(2t) .. M(2t+2),
+    // intervals 2t .. 2t+2.  M(2t-3) copies it into the stage tile t-3 left
+    // in interval 2t-4; M(2t-1) waits for it, and the barrier ending interval
+    // 2t-1 publishes it.  (tests/test_copy_schedule.py models both groups over
+    // every key extent up to 2560 and at 4k/32k/64k: each copy issued once
+    // into a free stage, complete and published before its first read, none
+    // in flight at the end.)
     issue_tile(0);
     if (ntile > 1) {
         issue_tile(1);
@@ -472,13 +474,12 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     phase_barrier();            // tile 0 visible
     read_v(smem, 0, vnext[0]);  // M(0): values of sub-tile 0 (times zero probabilities)
     read_v(smem, 1, vnext[1]);
-    if (grp) phase_barrier();   // group 1 starts one phase later
     // The wave in its matrix phase takes issue priority over the one in its
-    // softmax phase on the same SIMD, so the matrix core is fed first.
-    // The stage ring advances every second sub-tile; its offsets are carried
+    // softmax phase on the same SIMD, so the matrix core is fed first.  The
+    // stage ring advances every second sub-tile; its offsets are carried
     // through the loop rather than recomputed modulo the stage count.
     int so_j = 0, so_v = 0;
-    for (int j = 0; j <= nsub; ++j) {
+    auto m_and_copies = [&](int j) {
         __builtin_amdgcn_s_setprio(1);
         m_phase(j, so_j, so_v);
         if (j & 1) {
@@ -489,15 +490,26 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             if (tw + 1 < ntile) wait_copies<C::CPW>();
             else wait_copies<0>();
         }
-        phase_barrier();
         __builtin_amdgcn_s_setprio(0);
+    };
+    // Both groups run M(j) then V(j); group 0 ends interval j after V(j),
+    // group 1 after M(j), so interval j holds group 0's M(j), V(j) and group
+    // 1's V(j-1), M(j).
+    for (int j = 0; j <= nsub; ++j) {
+        m_and_copies(j);
+        if (grp) {
+            phase_barrier();
+            so_v = so_j;
+            if (j & 1) so_j = (so_j + C::STAGE == PP_NSTAGE * C::STAGE) ? 0 : so_j + C::STAGE;
+        }
         v_phase(j);
-        phase_barrier();
-        so_v = so_j;
-        if (j & 1) so_j = (so_j + C::STAGE == PP_NSTAGE * C::STAGE) ? 0 : so_j + C::STAGE;
+        if (!grp) {
+            phase_barrier();
+            so_v = so_j;
+            if (j & 1) so_j = (so_j + C::STAGE == PP_NSTAGE * C::STAGE) ? 0 : so_j + C::STAGE;
+        }
     }
     __builtin_amdgcn_s_setprio(0);
-    if (!grp) phase_barrier();  // matches group 1's extra barrier
 
     // ---- epilogue: combine the maps with lambda, optional RMS norm ----------
     if (my_row >= N) return;
@@ -581,9 +593,10 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t stream) {
 
 // ---------------------------------------------------------------------------
 // Map-split ping-pong (d = 128): 8 waves own 128 rows.  Wave w runs map
-// w >> 2 for row block w & 3; the map-2 waves form the second phase group,
-// one phase behind, so each SIMD holds the two maps of one row block, one in
-// its matrix phase while the other is in its softmax phase.  A wave keeps one
+// w >> 2 for row block w & 3; the map-2 waves form the second group (its
+// barrier sits between its matrix and softmax phases), so each SIMD holds the
+// two maps of one row block, one in its matrix phase while the other is in
+// its softmax phase.  A wave keeps one
 // map's query fragments and accumulator (d = 128 does not fit both).
 constexpr int PS_WAVES = 8;
 constexpr int PS_THREADS = WAVE * PS_WAVES;
@@ -847,7 +860,8 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
 #pragma unroll
     for (int u = 0; u < PS_PD; ++u)  // M(0): values of sub-tile 0 (times zero probabilities)
         read_v(smem, u, vnext[u]);
-    if (grp) phase_barrier();
+    // Intervals and barriers as in the d <= 64 kernel: the map-1 group ends
+    // interval j after V(j), the map-2 group after M(j).
     int so_j = 0, so_v = 0;   // stage ring offsets, carried as in the d <= 64 kernel
     for (int j = 0; j <= nsub; ++j) {
         __builtin_amdgcn_s_setprio(1);
@@ -860,15 +874,19 @@ prefill_ps_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
             if (tw + 1 < ntile) wait_copies<C::CPW>();
             else wait_copies<0>();
         }
-        phase_barrier();
         __builtin_amdgcn_s_setprio(0);
+        if (grp) {
+            phase_barrier();
+            so_v = so_j;
+            if (j & 1) so_j = (so_j + C::STAGE == PP_NSTAGE * C::STAGE) ? 0 : so_j + C::STAGE;
+        }
         v_phase(j);
-        phase_barrier();
-        so_v = so_j;
-        if (j & 1) so_j = (so_j + C::STAGE == PP_NSTAGE * C::STAGE) ? 0 : so_j + C::STAGE;
+        if (!grp) {
+            phase_barrier();
+            so_v = so_j;
+            if (j & 1) so_j = (so_j + C::STAGE == PP_NSTAGE * C::STAGE) ? 0 : so_j + C::STAGE;
+        }
     }
-    __builtin_amdgcn_s_setprio(0);
-    if (!grp) phase_barrier();
 
     // Epilogue: map-2 waves hand lambda-scaled accumulators to map-1 waves.
     const f32x2 hl = halves(lsum);

@@ -1,16 +1,18 @@
-"""Model of the fused prefill kernel's global->LDS copy schedule (the
-ping-pong kernel: two wave groups one phase apart, three LDS stages of 64-key
-tiles), checked over many key extents.
+"""Model of the fused prefill kernels' global->LDS copy schedule (the
+ping-pong kernels: two wave groups, three LDS stages of 64-key tiles), checked
+over many key extents.
 
 Rule under test, per wave of either group: before the loop, tiles 0 and 1 are
 issued and the wave waits for tile 0; at the end of its matrix phase of every
 odd step j it issues tile (j+3)/2 (if it exists) and then waits until at most
-CPW copies (tile (j+1)/2 + 1's, if that tile exists) are in flight.  Group g
-runs the matrix phase of step j in global phase 2j+g; every global phase ends
-with a workgroup barrier.  Invariants: every copy is issued once, into a stage
-whose previous tile (t-3) has no read left; a tile's copies of every wave are
-complete before the barrier that precedes its first read; nothing is in flight
-at the end.  Host-side logic only: no GPU.
+CPW copies (tile (j+1)/2 + 1's, if that tile exists) are in flight.  The loop
+has one workgroup barrier per step: group 0 places it after its softmax phase
+and group 1 between its matrix and softmax phases, so interval j (ending with
+the j-th loop barrier) holds the matrix phase of step j of both groups.
+Invariants: every copy is issued once, into a stage whose previous tile (t-3)
+was last read in an earlier interval; a tile's copies of every wave are
+complete in an interval before its first read; nothing is in flight at the
+end.  Host-side logic only: no GPU.
 """
 import pytest
 
@@ -36,7 +38,7 @@ def simulate(kv_end, cpw, tk=64, bn=32):
                     done_phase.setdefault((g, t), ph)
         mark(-1)
         for j in range(nsub + 1):
-            p = 2 * j + g
+            p = j                   # the interval of both groups' M(j)
             # The matrix phase of step j reads the keys of sub-tile j and the
             # values of sub-tile max(j-1, 0) (taking every step as visible).
             for t in {j // 2, max(j - 1, 0) // 2}:
