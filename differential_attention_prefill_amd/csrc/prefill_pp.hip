@@ -186,6 +186,12 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // This row block sees sub-tiles 0 .. jmax-1.
     const int jmax = __builtin_amdgcn_readfirstlane(
         wrow_last < wrow0 ? 0 : (causal ? min(nsub, wrow_last / BN + 1) : nsub));
+    // Sub-tiles j >= jmask need masking: they reach past the sequence end
+    // (j*BN + BN > N) or, causally, past the row block's first row
+    // (j*BN + BN - 1 > wrow0).
+    const int jmask = __builtin_amdgcn_readfirstlane(
+        min(N >= BN ? (N - BN) / BN + 1 : 0,
+            causal ? (wrow0 - BN + 1 < 0 ? 0 : (wrow0 - BN + 1) / BN + 1) : (1 << 30)));
 
     // Query fragments of both maps (B operand of S^T = K . Q^T): the lane
     // holds 8 consecutive elements of its row per 16-element k-step.
@@ -384,9 +390,9 @@ prefill_pp_kernel(const __bf16* __restrict__ q1, const __bf16* __restrict__ q2,
     // V(j): both online softmaxes of sub-tile j -> probabilities for M(j+1).
     auto v_phase = [&](int j) {
         if (j >= jmax) return;
-        const int kb = fresh(j * BN);
         // Rare (diagonal / last sub-tile), uniform: a real branch.
-        if (__builtin_expect((kb + BN > N) || (causal && kb + BN - 1 > wrow0), 0)) {
+        if (__builtin_expect(j >= jmask, 0)) {
+            const int kb = j * BN;
             // Register r holds key kb + key_of_reg(r) + 8*half, visible iff
             // that offset is below lim.
             const int lim = causal ? min(N - kb, my_row - kb + 1) : N - kb;

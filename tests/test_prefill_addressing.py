@@ -178,3 +178,27 @@ def test_largest_bf16_stride_fits_32_bit_offsets():
             assert (row * ld * 2 + chunk * 16).max() < 2 ** 31
         assert TK * ld * 2 < 2 ** 31
     assert TK * (1 << 24) * 2 >= 2 ** 31        # the first refused stride would not fit
+
+
+def first_masked_subtile(N, wrow0, causal, bn=32):
+    """The kernels' precomputed index of the first 32-key sub-tile that needs
+    masking, as they form it."""
+    j_end = (N - bn) // bn + 1 if N >= bn else 0
+    if not causal:
+        return j_end
+    x = wrow0 - bn + 1
+    return min(j_end, 0 if x < 0 else x // bn + 1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_first_masked_subtile_matches_the_masking_rule(causal):
+    # A sub-tile j needs masking iff it reaches past the sequence end
+    # (32j + 32 > N) or, causally, past the row block's first row
+    # (32j + 31 > first row); the kernels test j >= the precomputed index.
+    for N in list(range(1, 300)) + [4095, 4096, 4097]:
+        nsub = -(-N // 32)
+        for wrow0 in range(0, N, 32):
+            jm = first_masked_subtile(N, wrow0, causal)
+            for j in range(nsub + 1):
+                masked = (32 * j + 32 > N) or (causal and 32 * j + 31 > wrow0)
+                assert masked == (j >= jm), (N, wrow0, causal, j)
