@@ -17,6 +17,10 @@ What the kernels address:
   * Query fragments: flat 16-byte loads of the lane's own row (rows past N
     are not loaded).
   * Outputs: flat 16-byte stores of rows below N.
+
+Also the index of the first 32-key sub-tile a wave masks, which the d <= 64
+kernel computes once per wave: it must select exactly the sub-tiles the
+masking rule names, for every length and row block.
 """
 import itertools
 
