@@ -16,8 +16,11 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers (memory from hipMalloc or a
- *    caller's allocator such as PyTorch).  The library allocates nothing,
- *    keeps no state between calls, and never frees caller memory.
+ *    caller's allocator such as PyTorch).  The library allocates nothing and
+ *    never frees caller memory.  Between calls it keeps only per-device
+ *    caches (the CU count, a kernel's LDS limit, the address of the
+ *    allocation-free decode's fixed scratch array); no result of one call
+ *    depends on an earlier call.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued asynchronously; results are valid once the stream has
  *    reached that point.  Calls on different streams may run concurrently;
