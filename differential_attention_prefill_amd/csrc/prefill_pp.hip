@@ -583,9 +583,9 @@ template <int D, int DV, int MAPS>
 hipError_t launch_pp(const PrefillArgs& a, hipStream_t stream) {
     using C = PPCfg<D, DV, MAPS>;
     const int row_tiles = (a.N + PP_BM - 1) / PP_BM;
-    const int BH = a.B * a.H;
-    const int64_t blocks = (int64_t)BH * row_tiles;
+    const int64_t blocks = (int64_t)a.B * a.H * row_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const int BH = a.B * a.H;   // at most `blocks`, so it fits
     static std::atomic<bool> lds_ok[MAX_DEVICES];
     const hipError_t e = ensure_lds_limit(prefill_pp_kernel<D, DV, MAPS>, C::LDS, lds_ok);
     if (e != hipSuccess) return e;
@@ -955,9 +955,9 @@ template <int D, int DV, bool SK>
 hipError_t launch_ps(const PrefillArgs& a, hipStream_t stream) {
     using C = PSCfg<D, DV, SK>;
     const int row_tiles = (a.N + PS_BM - 1) / PS_BM;
-    const int BH = a.B * a.H;
-    const int64_t blocks = (int64_t)BH * row_tiles;
+    const int64_t blocks = (int64_t)a.B * a.H * row_tiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const int BH = a.B * a.H;   // at most `blocks`, so it fits
     static std::atomic<bool> lds_ok[MAX_DEVICES];
     const hipError_t e = ensure_lds_limit(prefill_ps_kernel<D, DV, SK>, C::LDS, lds_ok);
     if (e != hipSuccess) return e;
