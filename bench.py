@@ -15,6 +15,8 @@ HBM roofline, and the CPU oracle timed on a bounded sample of the same work.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import ctypes
 import json
 import os
 import sys
@@ -76,6 +78,40 @@ def profiled_traffic(kernel: str):
     return float(fields[kernel + "_traffic_bytes_per_launch"])
 
 
+class Ranges:
+    """roctx ranges around the bench's phases, from the ROCm profiler SDK's
+    roctx library: `rocprofv3 --marker-trace` shows them beside the kernels.
+    The ranges mark host-side enqueue intervals (launches are asynchronous).
+    Where the library is absent the ranges do nothing."""
+
+    def __init__(self):
+        self._lib = None
+        path = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib",
+                            "librocprofiler-sdk-roctx.so.1")
+        try:
+            lib = ctypes.CDLL(path)
+            lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+            lib.roctxRangePushA.restype = ctypes.c_int
+            lib.roctxRangePop.argtypes = []
+            lib.roctxRangePop.restype = ctypes.c_int
+            self._lib = lib
+        except (OSError, AttributeError):
+            pass
+
+    @contextlib.contextmanager
+    def __call__(self, name: str):
+        if self._lib is not None:
+            self._lib.roctxRangePushA(name.encode())
+        try:
+            yield
+        finally:
+            if self._lib is not None:
+                self._lib.roctxRangePop()
+
+
+RANGE = Ranges()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,34 +171,41 @@ def main():
     def step(record):
         if record:
             ev[0].record()
-        api.diffattn_lambda(*plam_in, layer=pcase.layer, out=plam)
-        api.diffattn_lambda(*dlam_in, layer=dcase.layer, out=dlam)
+        with RANGE("lambda"):
+            api.diffattn_lambda(*plam_in, layer=pcase.layer, out=plam)
+            api.diffattn_lambda(*dlam_in, layer=dcase.layer, out=dlam)
         if record:
             ev[1].record()
-        api.diffattn_prefill(q1, q2, k1, k2, v, plam, causal=pcase.causal, rmsnorm=pcase.rmsnorm,
-                             eps=pcase.eps, norm_scale=norm_scale, out=pout)
+        with RANGE("prefill"):
+            api.diffattn_prefill(q1, q2, k1, k2, v, plam, causal=pcase.causal,
+                                 rmsnorm=pcase.rmsnorm, eps=pcase.eps, norm_scale=norm_scale,
+                                 out=pout)
         if record:
             ev[2].record()
-        api.diffattn_decode(din["q"], din["k_cache"], din["v_cache"], din["seq_lens"], dlam,
-                            workspace=ws, out=dout)
+        with RANGE("decode"):
+            api.diffattn_decode(din["q"], din["k_cache"], din["v_cache"], din["seq_lens"], dlam,
+                                workspace=ws, out=dout)
         if record:
             ev[3].record()
 
-    for i in range(args.warmup):
-        step(False)
-        print("# warmup step %d done" % i, file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
+    with RANGE("warmup"):
+        for i in range(args.warmup):
+            step(False)
+            print("# warmup step %d done" % i, file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
 
     t_lam, t_pre, t_dec = [], [], []
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(True)
-        torch.cuda.synchronize()   # per-step sync keeps the event pairs readable
-        t_lam.append(ev[0].elapsed_time(ev[1]))
-        t_pre.append(ev[1].elapsed_time(ev[2]))
-        t_dec.append(ev[2].elapsed_time(ev[3]))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with RANGE("timed steps"):
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            with RANGE("step %d" % i):
+                step(True)
+                torch.cuda.synchronize()   # per-step sync keeps the event pairs readable
+            t_lam.append(ev[0].elapsed_time(ev[1]))
+            t_pre.append(ev[1].elapsed_time(ev[2]))
+            t_dec.append(ev[2].elapsed_time(ev[3]))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     print("# timed %d steps in %.3f s" % (args.steps, wall), file=sys.stderr, flush=True)
 
     ms_step = 1e3 * wall / args.steps
@@ -244,15 +287,17 @@ def main():
         for x in only:
             if x not in EXTRAS:
                 raise SystemExit("unknown extra %r (choose from %s)" % (x, ", ".join(EXTRAS)))
-        result["extras"] = measure_extras(dev, max(3, args.steps), set(only or EXTRAS))
+        with RANGE("extras"):
+            result["extras"] = measure_extras(dev, max(3, args.steps), set(only or EXTRAS))
         pin = din = None
 
     if not args.no_cpu_baseline:
         if pin is None:
             pin = W.make_prefill(pcase, device=dev)
             din = W.make_decode(dcase, device=dev)
-        result["cpu_baseline"] = cpu_baseline(pcase, pin, dcase, din, plam, dlam, norm_scale,
-                                              args.cpu_seconds)
+        with RANGE("cpu baseline"):
+            result["cpu_baseline"] = cpu_baseline(pcase, pin, dcase, din, plam, dlam, norm_scale,
+                                                  args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -278,18 +323,16 @@ EXTRAS = ("prefill_workloads", "v2_prefill", "unfused_vs_fused", "v1_decode", "b
 def measure_extras(dev, reps, which=frozenset(EXTRAS)):
     """Layouts measured beside the step, each on its own synthetic workload."""
     extras = {}
-    if "prefill_workloads" in which:
-        extras["prefill_workloads"] = _extra_prefill_workloads(dev, reps)
-    if "v2_prefill" in which:
-        extras["v2_prefill"] = _extra_v2_prefill(dev, reps)
-    if "unfused_vs_fused" in which:
-        extras["unfused_vs_fused"] = _extra_unfused(dev, reps)
-    if "v1_decode" in which:
-        extras["v1_decode"] = _extra_v1_decode(dev, reps)
-    if "baseline_decode" in which:
-        extras["baseline_decode"] = _extra_baseline_decode(dev, reps)
+    runs = (("prefill_workloads", _extra_prefill_workloads), ("v2_prefill", _extra_v2_prefill),
+            ("unfused_vs_fused", _extra_unfused), ("v1_decode", _extra_v1_decode),
+            ("baseline_decode", _extra_baseline_decode))
+    for name, fn in runs:
+        if name in which:
+            with RANGE("extras: " + name):
+                extras[name] = fn(dev, reps)
     if "snr_sweep" in which:
-        extras.update(_extra_snr(dev))
+        with RANGE("extras: snr_sweep"):
+            extras.update(_extra_snr(dev))
     return extras
 
 
