@@ -58,6 +58,16 @@ bool bf16_ld_ok(int64_t ldq, int64_t ldk, int64_t ldv) {
     return ldq <= BF16_MAX_LD && ldk <= BF16_MAX_LD && ldv <= BF16_MAX_LD;
 }
 
+// The kernels run 1-D grids of at most 2^31 - 1 workgroups, one per `rows`
+// query rows of one (b, h): at least 128 rows for the bf16 prefill kernels,
+// 32 for the fp32 kernel, 4 for the combine kernel.  The caller has bounded
+// B*H*N by 2^40, so the products stay in int64.
+constexpr int64_t MAX_GRID = 0x7fffffff;
+
+bool grid_fits(int B, int H, int N, int rows) {
+    return (int64_t)B * H * (((int64_t)N + rows - 1) / rows) <= MAX_GRID;
+}
+
 diffattn_status_t hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
     return fail(DIFFATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -134,6 +144,8 @@ diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k
                     (long long)BF16_MAX_LD);
     if ((int64_t)B * H * N > (int64_t)1 << 40)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill: B*H*N too large");
+    if (!grid_fits(B, H, N, dtype == DIFFATTN_BF16 ? 128 : 32))
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_prefill: B*H row tiles exceed the launch grid");
     for (int i = 0; i < 7; ++i) {
         diffattn_status_t s = check_device(ptrs[i], names[i]);
         if (s != DIFFATTN_OK) return s;
@@ -192,6 +204,9 @@ diffattn_status_t diffattn_prefill_v2(const void* q, const void* k, const void* 
                     dtype == DIFFATTN_BF16 ? "bf16" : "fp32");
     if ((int64_t)B * Hq * N > (int64_t)1 << 40)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_prefill_v2: B*Hq*N too large");
+    if (!grid_fits(B, Hq / 2, N, dtype == DIFFATTN_BF16 ? 128 : 32))
+        return fail(DIFFATTN_ERR_UNSUPPORTED,
+                    "diffattn_prefill_v2: B*Hq/2 row tiles exceed the launch grid");
     for (int i = 0; i < 5; ++i) {
         diffattn_status_t s = check_device(ptrs[i], names[i]);
         if (s != DIFFATTN_OK) return s;
@@ -249,6 +264,8 @@ diffattn_status_t diffattn_attention(const void* q, const void* k, const void* v
                     (long long)BF16_MAX_LD);
     if ((int64_t)B * H * N > (int64_t)1 << 40)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_attention: B*H*N too large");
+    if (!grid_fits(B, H, N, 128))
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_attention: B*H row tiles exceed the launch grid");
     for (int i = 0; i < 4; ++i) {
         diffattn_status_t s = check_device(ptrs[i], names[i]);
         if (s != DIFFATTN_OK) return s;
@@ -287,6 +304,8 @@ diffattn_status_t diffattn_combine(const float* o1, const float* o2, const float
         return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_combine: dv=%d not built", dv);
     if ((int64_t)B * H * N > (int64_t)1 << 40)
         return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "diffattn_combine: B*H*N too large");
+    if (!grid_fits(B, H, N, 4))
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_combine: B*H*N rows exceed the launch grid");
     for (int i = 0; i < 4; ++i) {
         diffattn_status_t s = check_device(ptrs[i], names[i]);
         if (s != DIFFATTN_OK) return s;

@@ -100,7 +100,10 @@ diffattn_status_t diffattn_lambda(const float* lq1, const float* lk1, const floa
  * UNSUPPORTED.  BF16 token strides ldq, ldk, ldv above 2^24 - 1 elements
  * also return UNSUPPORTED (the kernels address 64-row tiles with 32-bit byte
  * offsets).  Pointers must be 16-byte aligned and ld*sizeof(elem) a
- * multiple of 16 (INVALID_ARGUMENT otherwise).  B, H, N >= 1.
+ * multiple of 16 (INVALID_ARGUMENT otherwise).  B, H, N >= 1, and B*H*N at
+ * most 2^40 (INVALID_ARGUMENT otherwise).  The launch grid holds at most
+ * 2^31 - 1 workgroups: B*H*ceil(N/128) (BF16) or B*H*ceil(N/32) (FP32) above
+ * that returns UNSUPPORTED.
  */
 diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k1,
                                    const void* k2, const void* v, int64_t ldq, int64_t ldk,
@@ -121,7 +124,8 @@ diffattn_status_t diffattn_prefill(const void* q1, const void* q2, const void* k
  *   out    : device fp32 [B][Hq/2][N][D]
  * out[b,p,n] = (A1 - lambda_p A2) V with A1, A2 the softmaxes of the two
  * maps' scores / sqrt(D); causal != 0 restricts query n to keys 0..n.
- * Supported: BF16 and FP32 with D in {64, 128} (UNSUPPORTED otherwise).
+ * Supported: BF16 and FP32 with D in {64, 128} (UNSUPPORTED otherwise),
+ * with the size and grid limits of diffattn_prefill for H = Hq/2.
  * Hq must be a multiple of 2*Hkv, pointers 16-byte aligned, D*sizeof(elem)
  * a multiple of 16 (INVALID_ARGUMENT otherwise).  Asynchronous on stream.
  */
@@ -138,7 +142,8 @@ diffattn_status_t diffattn_prefill_v2(const void* q, const void* k, const void* 
  * Layouts as for diffattn_prefill: q, k [B][H][N][ld] with d columns, v with
  * dv columns, out fp32 [B][H][N][dv].  causal != 0: query n sees keys 0..n.
  * Supported: BF16 with (d, dv) in {(64,128), (64,64)}; FP32 and other
- * shapes return UNSUPPORTED, as do token strides above 2^24 - 1 elements.
+ * shapes return UNSUPPORTED, as do token strides above 2^24 - 1 elements
+ * and the BF16 grid limit of diffattn_prefill.
  * Other errors as for diffattn_prefill.
  */
 diffattn_status_t diffattn_attention(const void* q, const void* k, const void* v, int64_t ldq,
@@ -151,7 +156,8 @@ diffattn_status_t diffattn_attention(const void* q, const void* k, const void* v
  * fp32 [B][H][N][dv] tensors (page "差分注意力", part 一 "差分思路"), then the
  * optional RMS norm exactly as in diffattn_prefill.  lambda: device fp32 [H].
  * out may alias o1.  Supported dv: 64, 128 (UNSUPPORTED otherwise); pointers
- * 4-byte aligned (INVALID_ARGUMENT otherwise).
+ * 4-byte aligned (INVALID_ARGUMENT otherwise).  B*H*N at most 2^40
+ * (INVALID_ARGUMENT), and B*H*ceil(N/4) at most 2^31 - 1 (UNSUPPORTED).
  */
 diffattn_status_t diffattn_combine(const float* o1, const float* o2, const float* lambda, int B,
                                    int H, int N, int dv, int rmsnorm, float eps, float norm_scale,

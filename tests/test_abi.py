@@ -265,6 +265,34 @@ def test_attention_stride_limit(lib, kw, code):
     assert _attention(lib, **kw) == code
 
 
+# Every launch is a 1-D grid of at most 2^31 - 1 workgroups, one per row tile
+# of one (b, h): 128 rows or more for the bf16 kernels, 32 for fp32, 4 for the
+# combine.  Sizes whose row tiles would not fit are refused before any launch
+# (UNSUPPORTED); one tile fewer passes this check and then fails the
+# device-pointer check on the fake address (INVALID_ARGUMENT).
+@pytest.mark.parametrize("fn,kw,code", [
+    (_prefill, dict(B=1 << 16, H=1 << 15, N=128), UNSUPPORTED),
+    (_prefill, dict(B=(1 << 16) - 1, H=1 << 15, N=128), INVALID),
+    (_prefill, dict(dtype=0, B=1 << 16, H=1 << 13, N=128), UNSUPPORTED),
+    (_prefill, dict(dtype=0, B=(1 << 16) - 1, H=1 << 13, N=128), INVALID),
+    (_prefill_v2, dict(B=1 << 16, Hq=1 << 16, Hkv=1, N=128), UNSUPPORTED),
+    (_prefill_v2, dict(B=(1 << 16) - 1, Hq=1 << 16, Hkv=1, N=128), INVALID),
+    (_attention, dict(B=1 << 16, H=1 << 15, N=128), UNSUPPORTED),
+    (_attention, dict(B=(1 << 16) - 1, H=1 << 15, N=128), INVALID),
+])
+def test_launch_grid_limit(lib, fn, kw, code):
+    assert fn(lib, **kw) == code
+    if code == UNSUPPORTED:
+        assert "grid" in lib.diffattn_last_error().decode()
+
+
+@pytest.mark.parametrize("B,code", [(1 << 16, UNSUPPORTED), ((1 << 16) - 1, INVALID)])
+def test_combine_grid_limit(lib, B, code):
+    # B*H*ceil(N/4) = B * 2^15: 2^31 is one past the grid limit.
+    assert lib.diffattn_combine(FAKE, FAKE, FAKE, B, 1 << 14, 8, 128, 0, 1e-5, 1.0, None, FAKE,
+                                None) == code
+
+
 # The Python binding checks shapes, dtypes and devices before it calls the
 # library (CPU tensors: a call that passes these checks is then refused by the
 # library's device-pointer check, as DiffAttnError).
