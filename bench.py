@@ -316,14 +316,15 @@ def _time_launches(fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-EXTRAS = ("prefill_workloads", "v2_prefill", "unfused_vs_fused", "v1_decode", "baseline_decode",
-          "snr_sweep")
+EXTRAS = ("prefill_workloads", "prefill_length_sweep", "v2_prefill", "unfused_vs_fused",
+          "v1_decode", "baseline_decode", "snr_sweep")
 
 
 def measure_extras(dev, reps, which=frozenset(EXTRAS)):
     """Layouts measured beside the step, each on its own synthetic workload."""
     extras = {}
-    runs = (("prefill_workloads", _extra_prefill_workloads), ("v2_prefill", _extra_v2_prefill),
+    runs = (("prefill_workloads", _extra_prefill_workloads),
+            ("prefill_length_sweep", _extra_prefill_length_sweep), ("v2_prefill", _extra_v2_prefill),
             ("unfused_vs_fused", _extra_unfused), ("v1_decode", _extra_v1_decode),
             ("baseline_decode", _extra_baseline_decode))
     for name, fn in runs:
@@ -377,6 +378,36 @@ def _extra_prefill_workloads(dev, reps):
         del inp, out
         torch.cuda.empty_cache()
     return per_cfg
+
+
+def _extra_prefill_length_sweep(dev, reps):
+    """The fused V1 prefill (the step's kernel and norm) at other lengths,
+    4k to 128k, on plain unit-variance inputs: its rate against N."""
+    import torch
+
+    from differential_attention_prefill_amd import api
+    from differential_attention_prefill_amd import workloads as W
+
+    per_len = {}
+    for c in W.V1_LENGTH_SWEEP:
+        print("# extras: %s" % c.name, file=sys.stderr, flush=True)
+        inp = W.make_prefill(c, device=dev)
+        lam = api.diffattn_lambda(*(inp[x].contiguous() for x in ("lq1", "lk1", "lq2", "lk2")),
+                                  layer=c.layer)
+        scale = 1.0 - api.diffattn_lambda_init(c.layer)
+        out = torch.empty((c.B, c.H, c.N, c.dv), dtype=torch.float32, device=dev)
+        n = max(reps, 20) if c.N <= 16384 else max(3, reps // 2)
+        ms = _time_launches(lambda: api.diffattn_prefill_packed(
+            inp["q"], inp["k"], inp["v"], lam, causal=c.causal, rmsnorm=c.rmsnorm, eps=c.eps,
+            norm_scale=scale, out=out), n)
+        f = prefill_flops(c)
+        per_len[c.name] = {"N": c.N, "H": c.H, "avg_launch_ms": round(ms, 4),
+                           "algorithmic_flops_per_launch": f,
+                           "achieved_tflops": round(f / (ms * 1e-3) / 1e12, 2),
+                           "frac_of_bf16_peak": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del inp, out
+        torch.cuda.empty_cache()
+    return per_len
 
 
 def _extra_v2_prefill(dev, reps):
@@ -494,7 +525,7 @@ def _extra_v1_decode(dev, reps):
     scale = 1.0 - api.diffattn_lambda_init(c.layer)
     ms = _time_launches(lambda: api.diffattn_decode_v1(
         inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"], lam, rmsnorm=True, eps=c.eps,
-        norm_scale=scale, workspace=ws, out=out), reps)
+        norm_scale=scale, workspace=ws, out=out), max(reps, 20))
     lens = inp["seq_lens"].cpu().tolist()
     nbytes = float(sum(int(x) for x in lens)) * c.H * (2 * c.d + c.dv) * 2 + \
         c.B * c.H * (2 * c.d * 2 + c.dv * 4) + c.H * 4 + c.B * 4

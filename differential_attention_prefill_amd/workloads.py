@@ -154,6 +154,15 @@ V2_PREFILL_32K = V2PrefillCase("v2_prefill_bf16_b1_hq32_hkv8_n32768_d128", "bf16
 V1_DECODE = V1DecodeCase("v1_decode_bf16_b16_h16_d64_dv128_l4096_65536", B=16, H=16, d=64, dv=128,
                          Lmin=4096, Lmax=65536, layer=12, seed=7)
 
+# The V1 layout with the 64k workload's norm at other lengths (no needles), for
+# the fused kernel's rate against N: from below the long workloads to twice the
+# longest.  Each length takes a different head count, so every launch has its
+# own workgroup count (N/256 row tiles per head).
+V1_LENGTH_SWEEP = tuple(
+    PrefillCase("v1_sweep_bf16_b1_h%d_n%d_d64_dv128" % (h, n), "bf16", B=1, H=h, N=n, d=64,
+                dv=128, layer=12, rmsnorm=True, seed=8)
+    for n, h in ((4096, 48), (8192, 32), (16384, 24), (131072, 8)))
+
 PREFILL_CASES = {c.name: c for c in (TINY_FP32, V1_NORM, NEEDLE_32K, MULTI_NEEDLE_64K)}
 DECODE_CASES = {V2_DECODE.name: V2_DECODE}
 

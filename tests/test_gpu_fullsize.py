@@ -12,6 +12,8 @@ back finite (a tile that no workgroup writes cannot pass).  Then:
     the needle rows, against the oracle;
   * V2 prefill at 32k, D = 128: the first, last and one random row of every
     128-row tile of every pair.
+  * the length-sweep workloads at 8k (every row) and 128k (the first, last
+    and one random row of every 256-row tile of every head).
 
 The oracle runs on all host threads; each test prints its case first.
 """
@@ -137,3 +139,28 @@ def test_v2_prefill_32k_every_tile():
     ref = oracle.prefill(q[:, 0::2].contiguous(), q[:, 1::2].contiguous(), k, k, v,
                          lam_gpu.cpu().numpy(), causal=case.causal, rows=rows)
     compare(got, ref, "bf16", case.name + " (every tile)")
+
+
+@pytest.mark.parametrize("n", [8192, 131072])
+def test_length_sweep_against_oracle(n):
+    """The length-sweep workloads the benchmark times beside the step: at 8k
+    every row of every head, at 128k the first, last and one random row of
+    every 256-row tile of every head."""
+    _require_gpu()
+    case = next(c for c in W.V1_LENGTH_SWEEP if c.N == n)
+    say("length sweep %s: GPU run into a NaN-filled output" % case.name)
+    inp = W.make_prefill(case, device=DEV)
+    lam_gpu = gpu_lambda(inp, case.layer)
+    out = _run_nan_filled(case, inp, lam_gpu)
+    heads = case.B * case.H
+    if n <= 8192:
+        rows = np.arange(heads * case.N, dtype=np.int64)
+    else:
+        rows = _tile_rows(heads, case.N, 256, per_tile=1, seed=n)
+        assert np.unique(rows // 256).size == heads * case.N // 256
+    got = out.reshape(-1, case.dv)[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    del out
+    host = {k: inp[k].cpu() for k in ("q", "k", "v")}
+    say("length sweep %s: %d rows against the oracle" % (case.name, rows.size))
+    ref = run_prefill_oracle(case, host, lam_gpu.cpu().numpy(), rows=rows)
+    compare(got, ref, "bf16", "%s (%s)" % (case.name, "every row" if n <= 8192 else "every tile"))
