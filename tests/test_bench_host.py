@@ -49,3 +49,48 @@ def test_decode_bytes_and_flops_count_every_row_once():
     extra = c.B * c.Hq * c.D * 2 + (c.Hq // 2) * 4 + c.B * 4 + c.B * (c.Hq // 2) * c.D * 4
     assert bench.decode_bytes(c, lens) == kv + extra
     assert bench.decode_flops(c, lens) == sum(int(L) for L in lens) * (c.Hq // 2) * 6 * c.D
+
+
+def test_ranges_nest_and_do_nothing_without_the_roctx_library(monkeypatch):
+    # With the library the ranges push and pop in pairs; without it (no ROCm
+    # profiler SDK under ROCM_PATH) every range is a no-op and the body runs.
+    calls = []
+
+    class FakeLib:
+        def roctxRangePushA(self, name):
+            calls.append(("push", name))
+            return 0
+
+        def roctxRangePop(self):
+            calls.append(("pop",))
+            return 0
+
+    r = bench.Ranges()
+    r._lib = FakeLib()
+    with r("outer"):
+        with r("inner"):
+            pass
+    assert calls == [("push", b"outer"), ("push", b"inner"), ("pop",), ("pop",)]
+    try:
+        with r("raises"):
+            raise KeyError("x")
+    except KeyError:
+        pass
+    assert calls[-1] == ("pop",)          # popped on the way out of an exception
+
+    monkeypatch.setenv("ROCM_PATH", "/nonexistent-rocm")
+    empty = bench.Ranges()
+    assert empty._lib is None
+    ran = []
+    with empty("anything"):
+        ran.append(1)
+    assert ran == [1]
+
+
+def test_every_extra_has_a_runner():
+    # measure_extras runs each name in EXTRAS; a name with no runner would be
+    # silently skipped.
+    import inspect
+    src = inspect.getsource(bench.measure_extras)
+    for name in bench.EXTRAS:
+        assert '"%s"' % name in src, name
